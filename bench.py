@@ -1,0 +1,211 @@
+"""Benchmark of the paged QK-norm + RoPE + GQA attention step on one MI355X.
+
+One step = the whole path over one batch: qknorm_rope_append over every token
+(prompt chunks + decode rows), paged_prefill_attn over the prompt tokens,
+paged_decode_attn over the decode rows, all on one stream. The default
+workload is the mixed step (2 prompt chunks of 2048 tokens at positions 8192
+and 0, 128 decode rows at positions uniform in [1, 16384], 65536-page bfloat16
+pool), the one workload that exercises every part of the path.
+
+Prints one JSON line. ``value`` is the paged-decode attention throughput in
+algorithmic GB/s (K/V bytes of every visible position + q + out, divided by the
+decode kernel's time, measured with HIP events on the launch stream over the
+timed steps); the prefill TFLOP/s (visible (query, key) pairs x 16384 FLOP) and
+the append GB/s are reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def algorithmic_work(w):
+    """Bytes / FLOPs each part of one step must move or compute."""
+    import numpy as np
+    D, HQ, HKV = 128, 32, 8
+    dec_pos = w.step_positions.astype(np.int64)
+    R = len(dec_pos)
+    dec_kv = int((dec_pos + 1).sum()) * HKV * D * 2 * 2          # K and V, bf16
+    dec_bytes = dec_kv + R * HQ * D * 2 + R * HQ * D * 4 + R * 4 * (1 + w.pages_per_row)
+    pre_pairs = int((w.positions.astype(np.int64) + 1).sum())
+    pre_flops = pre_pairs * 4 * D * HQ
+    n = w.n_tokens
+    app_bytes = n * ((HQ + 2 * HKV) * D * 2 * 2 + D * 4 + 4 + 4)  # q,k,v in + q_out,k,v out, cos/sin, pos, slot
+    return {"decode_bytes": dec_bytes, "decode_kv_bytes": dec_kv, "prefill_flops": pre_flops,
+            "prefill_pairs": pre_pairs, "append_bytes": app_bytes}
+
+
+def cpu_baseline(w, sample_rows=64, seed=0):
+    """Oracle decode of a bounded sample of the workload's decode rows on the host cores.
+
+    The sampled rows' pool contents are materialised (outside the timed region)
+    in a compact pool with an identity page table; the timed region is the
+    oracle's decode of those rows.
+    """
+    import numpy as np
+    import oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    rng = np.random.default_rng(seed)
+    rows = sorted(rng.choice(w.n_decode, size=min(sample_rows, w.n_decode), replace=False).tolist())
+    P = w.n_prefill
+    every_at = np.concatenate([w.positions, w.step_positions]).astype(np.int64)
+    sel = [P + b for b in rows]
+    q_out, k_rows, v_rows = O.append(w.q[sel], w.k[sel], w.v[sel], w.dtype, w.dtype,
+                                     w.q_gain, w.k_gain, every_at[sel])
+    pos_s = w.step_positions[rows].astype(np.int64)
+    ppr = -(-(int(pos_s.max()) + 1) // 64)
+    table = np.arange(len(rows) * ppr, dtype=np.int32).reshape(len(rows), ppr)
+    kp = np.zeros((8, len(rows) * ppr * 64, 128), np.uint16)
+    vp = np.zeros_like(kp)
+    for i, b in enumerate(rows):
+        n = int(pos_s[i])          # history positions 0..n-1, then the row's new token
+        slots = w.row_slot_list(w.decode_row0 + b, n)
+        base = i * ppr * 64
+        for g in range(8):
+            kp[g, base:base + n] = W.host_history(w, 0, g, slots)
+            vp[g, base:base + n] = W.host_history(w, 1, g, slots)
+        kp[:, base + n] = k_rows[i]
+        vp[:, base + n] = v_rows[i]
+    t0 = time.perf_counter()
+    O.decode(q_out, w.dtype, kp, vp, w.dtype, table, pos_s, W.SCALE)
+    dt = time.perf_counter() - t0
+    nbytes = int((pos_s + 1).sum()) * 8 * 128 * 2 * 2
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"float64 oracle decode of {len(rows)} of the {w.n_decode} decode rows "
+                      f"({int((pos_s + 1).sum())} visible positions, {nbytes / 1e9:.3f} GB of K/V)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4, help="standard workload index (default: mixed step)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path has no "
+              "cross-GPU part; see the sharding notes in the design document.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import qk_norm_rope_amd as Q
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    w = W.config(args.workload)
+    if w.dtype != "bf16":
+        print("bench.py measures the bfloat16 workloads (1..4)", file=sys.stderr)
+        sys.exit(2)
+    t = W.upload(w, dev)
+    k_pool, v_pool = W.make_pools(w, dev)
+    cos, sin = Q.rope_table(1e6, W.MAX_POSITIONS)
+    cos, sin = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
+    P, R = w.n_prefill, w.n_decode
+    positions_all = torch.cat([t["positions"], t["step_positions"]])
+    q_out = torch.empty((P + R, 4096), dtype=torch.bfloat16, device=dev)
+    pre_out = torch.empty((max(P, 1), 4096), dtype=torch.float32, device=dev)
+    dec_out = torch.empty((max(R, 1), 4096), dtype=torch.float32, device=dev)
+    ws_p = torch.zeros(max(1, Q.prefill_workspace_bytes(k_pool, 32, max(P, 1))), dtype=torch.uint8, device=dev)
+    ws_d = torch.zeros(max(1, Q.decode_workspace_bytes(k_pool, 32, max(R, 1), w.pages_per_row)),
+                       dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step(timed):
+        if timed:
+            ev[0].record(stream)
+        Q.qknorm_rope_append(t["q"], t["k"], t["v"], t["q_gain"], t["k_gain"], cos, sin, positions_all,
+                             q_out, k_pool, v_pool, slots=t["slots"] if P else None,
+                             table=t["decode_table"] if R else None)
+        if timed:
+            ev[1].record(stream)
+        if P:
+            Q.paged_prefill_attn(q_out[:P], k_pool, v_pool, t["table"], t["rows"], t["positions"],
+                                 W.SCALE, pre_out, ws_p)
+        if timed:
+            ev[2].record(stream)
+        if R:
+            Q.paged_decode_attn(q_out[P:], k_pool, v_pool, t["decode_table"], t["step_positions"],
+                                W.SCALE, dec_out, ws_d)
+        if timed:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    times = {"append": 0.0, "prefill": 0.0, "decode": 0.0}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        # per-kernel windows come from the events of each step
+        ev[3].synchronize()
+        times["append"] += ev[0].elapsed_time(ev[1])
+        times["prefill"] += ev[1].elapsed_time(ev[2])
+        times["decode"] += ev[2].elapsed_time(ev[3])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for k in times:
+        times[k] /= args.steps  # ms per launch
+    step_ms = sum(times.values())
+
+    work = algorithmic_work(w)
+    dec_gbs = work["decode_bytes"] / (times["decode"] * 1e-3) / 1e9 if R else 0.0
+    pre_tflops = work["prefill_flops"] / (times["prefill"] * 1e-3) / 1e12 if P else 0.0
+    app_gbs = work["append_bytes"] / (times["append"] * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(dec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "prefill_tokens": P, "decode_rows": R,
+                   "prefill_chunks": "2x2048 at positions 8192 and 0" if args.workload == 4 else None,
+                   "decode_positions": "uniform [1, 16384]" if args.workload == 4 else None,
+                   "pool_pages": w.num_pages, "page_size": 64, "q_heads": 32, "kv_heads": 8,
+                   "head_dim": 128},
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_decode_bf16_kernel",
+                     "bytes_per_launch": work["decode_bytes"], "ms_per_launch": round(times["decode"], 5)},
+        "prefill": {"tflops": round(pre_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "frac": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": work["prefill_flops"],
+                    "ms_per_launch": round(times["prefill"], 5), "bound": "mfma"},
+        "append": {"gbs": round(app_gbs, 2), "frac": round(app_gbs / HBM_PEAK_GBS, 4),
+                   "bytes_per_launch": work["append_bytes"], "ms_per_launch": round(times["append"], 5),
+                   "bound": "hbm"},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * qknr.h -- C ABI of libqknr: paged QK-norm + RoPE + grouped-query attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the attention step of a Qwen3-style decoder serving from a
+ * paged KV cache, as the nest "models/qwen3-8b/files" page states them
+ * (README: architecture paragraph and Entries table; src/attention.linnet:
+ * decode_paged, prefill_paged, step_paged, split_heads; src/norm.linnet;
+ * src/rope.linnet), with the loop form of fantasma "src/inference/model.zig"
+ * (fullAttentionForward, applyRope).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Every call only enqueues work on that stream; nothing synchronises, nothing
+ *   allocates device memory, and the library keeps no state between calls, so
+ *   calls are thread-safe. Ordering (append before attention) comes from the
+ *   stream.
+ * - Ownership: the caller owns every buffer. Device pointers must stay valid
+ *   until the enqueued work has finished.
+ * - Activations are token-major: q is [n][num_q_heads*head_dim] and k, v are
+ *   [n][num_kv_heads*head_dim]; head h occupies columns h*head_dim ..
+ *   h*head_dim+head_dim-1 (attention.linnet, split_heads / merge_heads).
+ * - Pools: k_pool and v_pool are [num_kv_heads][num_pages*page_size][head_dim]
+ *   in the pool dtype (cache_k / cache_v of attention.linnet with Batch = 1:
+ *   one row that is a pool of pages). Position p of a row whose page list is
+ *   table[r][0..pages_per_row) lives in slot table[r][p / page_size]*page_size
+ *   + p % page_size (Entries table, decode_paged).
+ * - Tables are int32 [n_table_rows][pages_per_row], row-major.
+ * - Positions are 0-based. A query at position p sees positions 0..p of its
+ *   row, its own included (attention.linnet, decode: keys up to and including
+ *   the query's position).
+ * - Query head h reads KV head h / (num_q_heads / num_kv_heads) (model.zig,
+ *   fullAttentionForward).
+ * - Errors: a negative qkr_status is returned before anything is enqueued when
+ *   an argument is invalid; QKR_ELAUNCH when the runtime refuses a launch.
+ *   Device-side data (page ids, positions, slots, rows) is not validated
+ *   against the caller's intent, but every index the kernels form is range
+ *   checked: an out-of-range page id, position, row or slot makes that token's
+ *   or row's output unspecified (it is skipped or reads nothing), never an
+ *   out-of-bounds access.
+ * - The kernels are built for head_dim 128 and page_size 64; other values
+ *   return QKR_EUNSUPPORTED.
+ */
+#ifndef QKNR_H
+#define QKNR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { QKR_F32 = 0, QKR_BF16 = 1 } qkr_dtype;
+
+typedef enum {
+  QKR_OK = 0,
+  QKR_EINVAL = -1,          /* null pointer, negative count, bad divisibility  */
+  QKR_EUNSUPPORTED = -2,    /* head_dim != 128, page_size != 64, dtype combo    */
+  QKR_EWORKSPACE = -3,      /* workspace missing or smaller than required       */
+  QKR_ELAUNCH = -4          /* the HIP runtime reported an error on launch      */
+} qkr_status;
+
+/* Shape of the paged pool. num_q_heads % num_kv_heads == 0 and the group size
+ * num_q_heads / num_kv_heads must be 4 for the bfloat16 attention kernels
+ * (attention.linnet where-clause: Heads % KvHeads == 0). */
+typedef struct qkr_pool {
+  int32_t num_q_heads;   /* 32 for Qwen3-8B                                   */
+  int32_t num_kv_heads;  /* 8 for Qwen3-8B                                    */
+  int32_t head_dim;      /* 128                                               */
+  int32_t page_size;     /* 64                                                */
+  int64_t num_pages;     /* pool capacity in pages                            */
+  int32_t dtype;         /* qkr_dtype of k_pool, v_pool and q_out             */
+  int32_t reserved;      /* must be 0                                         */
+} qkr_pool;
+
+/*
+ * qknorm_rope_append -- QK-norm, RoPE and the cache write for n_tokens tokens.
+ *
+ * For every token t and every query head / KV head slice x (head_dim wide):
+ *   y = x * (mean(x^2) + eps)^(-1/2) * gain   (gain = q_gain or k_gain, shared
+ *                                              by all heads; norm.linnet with
+ *                                              eps 1e-6, applied after the
+ *                                              split into heads, README)
+ *   then RoPE at positions[t]: element i and i + head_dim/2 rotate by the angle
+ *   whose cosine/sine are rope_cos/rope_sin[positions[t]][i] (model.zig,
+ *   applyRope; rope.linnet, tables).
+ * Rotated q goes to q_out[t] (pool dtype). Rotated k and raw v (only cast to the
+ * pool dtype) go to slot s of every KV head of k_pool / v_pool, where
+ *   s = slots[t]                                   for t <  n_slotted
+ *     (prefill_paged: the caller gives each prompt token its slot), and
+ *   s = table[b][p / 64]*64 + p % 64, b = t - n_slotted, p = positions[t]
+ *                                                  for t >= n_slotted
+ *     (decode_paged: row b's slot from its page table).
+ * A negative slot skips the write (padding). This covers step_paged's single
+ * norm + rope + write over prompt tokens followed by decode rows.
+ *
+ * The float32 arithmetic is fixed so that q_out and the written pool bytes are
+ * reproducible bit for bit: squares summed in pairs (i, i+64), then a pairwise
+ * tree over i, mean by an exact /128, r = 1/sqrt(ms + eps) correctly rounded,
+ * y = (x*r)*g, rotation without fused multiply-add, round-to-nearest-even store.
+ *
+ * q, k, v      : device, in_dtype, shapes above.
+ * q_gain/k_gain: device float32 [head_dim].
+ * rope_cos/sin : device float32 [rope_rows][head_dim/2] (see qkr_rope_table).
+ * positions    : device int32 [n_tokens], each in [0, rope_rows).
+ * slots        : device int32 [n_slotted] (may be NULL when n_slotted == 0).
+ * table        : device int32 [n_tokens - n_slotted][pages_per_row] (may be NULL
+ *                when n_slotted == n_tokens).
+ * q_out        : device, pool dtype, [n_tokens][num_q_heads*head_dim].
+ * n_tokens == 0 is a no-op.
+ */
+int qknorm_rope_append(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                       const void* q, const void* k, const void* v, int32_t in_dtype,
+                       const float* q_gain, const float* k_gain, float eps,
+                       const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                       const int32_t* positions,
+                       const int32_t* slots, int32_t n_slotted,
+                       const int32_t* table, int32_t pages_per_row,
+                       void* q_out, void* k_pool, void* v_pool);
+
+/*
+ * paged_decode_attn -- one query token per row over that row's pages
+ * (attention.linnet, decode_paged / paged_attention).
+ *
+ * Row b's query q[b] (pool dtype, [n_rows][num_q_heads*head_dim], normally the
+ * q_out of qknorm_rope_append) attends with each query head over positions
+ * 0..positions[b] of table row b:
+ *   out[b][h] = sum_j softmax_j(scale * <q_bh, K_j>) V_j
+ * out is float32 [n_rows][num_q_heads*head_dim]. The work is split over page
+ * ranges (flash decoding) and the partial softmax states are merged exactly;
+ * the split depends only on positions, so the result does not depend on where
+ * the pages sit in the pool.
+ *
+ * workspace: device memory of at least paged_decode_attn_workspace() bytes. It
+ * must be zero-filled before its first use; every call leaves it ready for the
+ * next (its counters return to zero). Calls that share a workspace must be
+ * ordered on one stream.
+ */
+int paged_decode_attn(void* stream, const qkr_pool* pool, int32_t n_rows,
+                      const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* table, int32_t pages_per_row,
+                      const int32_t* positions, float scale, float* out,
+                      void* workspace, size_t workspace_bytes);
+
+size_t paged_decode_attn_workspace(const qkr_pool* pool, int32_t n_rows, int32_t pages_per_row);
+
+/*
+ * paged_prefill_attn -- packed prompt tokens over their rows' pages
+ * (attention.linnet, prefill_paged / paged_prefill_attention).
+ *
+ * Token p (query q[p], row rows[p], position positions[p]) attends with each
+ * query head over positions 0..positions[p] of table row rows[p]; the keys of
+ * the pass itself are already in the pool (the append runs first), so a chunk
+ * sees its own earlier tokens and any history or shared pages before it.
+ * Prompts are packed end to end; the kernel tiles the pack in blocks of 64
+ * tokens and handles blocks that span several rows.
+ *
+ * rows, positions: device int32 [n_tokens]; rows[p] in [0, n_table_rows).
+ * out: float32 [n_tokens][num_q_heads*head_dim].
+ * workspace: at least paged_prefill_attn_workspace() bytes (holds the tile
+ * schedule); contents need no initialisation.
+ */
+int paged_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                       const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
+                       const int32_t* rows, const int32_t* positions,
+                       float scale, float* out, void* workspace, size_t workspace_bytes);
+
+size_t paged_prefill_attn_workspace(const qkr_pool* pool, int32_t n_tokens);
+
+/*
+ * qkr_rope_table -- host helper: the RoPE cos/sin table (host memory).
+ * For pos < rope_rows and i < head_dim/2:
+ *   inv = 1 / theta^(2i/head_dim), a = pos*inv (double precision),
+ *   cos_out[pos][i] = (float)cos(a), sin_out[pos][i] = (float)sin(a)
+ * (model.zig, loadWeights; rope.linnet, tables with THETA = 1e6). Only half the
+ * width is stored because both halves of a head use the same frequencies.
+ */
+int qkr_rope_table(double theta, int32_t rope_rows, int32_t head_dim,
+                   float* cos_out, float* sin_out);
+
+/* Human-readable name of a qkr_status value. */
+const char* qkr_status_str(int status);
+
+/* Text of the HIP runtime error behind the calling thread's last QKR_ELAUNCH
+ * ("" if none). The pointer stays valid until the thread's next failing call. */
+const char* qkr_last_error(void);
+
+/* Library version, as MAJOR*10000 + MINOR*100 + PATCH. */
+int qkr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKNR_H */

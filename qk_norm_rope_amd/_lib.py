@@ -1,0 +1,230 @@
+"""ctypes binding of libqknr (include/qknr.h). Argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, checks dtype,
+shape and contiguity, and passes raw pointers and the current HIP stream to the
+C ABI. All computation happens in the library's kernels; if the library is not
+built the import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqknr.so")
+
+QKR_F32 = 0
+QKR_BF16 = 1
+HEAD_DIM = 128
+PAGE_SIZE = 64
+
+EXPORTED = (
+    "qknorm_rope_append",
+    "paged_decode_attn",
+    "paged_decode_attn_workspace",
+    "paged_prefill_attn",
+    "paged_prefill_attn_workspace",
+    "qkr_rope_table",
+    "qkr_status_str",
+    "qkr_last_error",
+    "qkr_version",
+)
+
+
+class Pool(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class QknrError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        detail = LIB.qkr_last_error().decode() if status == -4 else ""
+        super().__init__(f"{where}: {status_str(status)} ({status}){': ' + detail if detail else ''}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m qk_norm_rope_amd.build`")
+    # PyTorch ships its own HIP runtime (soname libamdhip64.so.7). Loading torch
+    # first makes the library's libamdhip64.so.7 dependency resolve to that same
+    # runtime, so torch's streams and allocations are valid in the library's
+    # calls; two HIP runtimes in one process do not share devices.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    pool_p = ctypes.POINTER(Pool)
+    lib.qknorm_rope_append.restype = ctypes.c_int
+    lib.qknorm_rope_append.argtypes = [vp, pool_p, i32, vp, vp, vp, i32, vp, vp, f32, vp, vp, i32,
+                                       vp, vp, i32, vp, i32, vp, vp, vp]
+    lib.paged_decode_attn.restype = ctypes.c_int
+    lib.paged_decode_attn.argtypes = [vp, pool_p, i32, vp, vp, vp, vp, i32, vp, f32, vp, vp, sz]
+    lib.paged_decode_attn_workspace.restype = sz
+    lib.paged_decode_attn_workspace.argtypes = [pool_p, i32, i32]
+    lib.paged_prefill_attn.restype = ctypes.c_int
+    lib.paged_prefill_attn.argtypes = [vp, pool_p, i32, vp, vp, vp, vp, i32, i32, vp, vp, f32, vp, vp, sz]
+    lib.paged_prefill_attn_workspace.restype = sz
+    lib.paged_prefill_attn_workspace.argtypes = [pool_p, i32]
+    lib.qkr_rope_table.restype = ctypes.c_int
+    lib.qkr_rope_table.argtypes = [ctypes.c_double, i32, i32, vp, vp]
+    lib.qkr_status_str.restype = ctypes.c_char_p
+    lib.qkr_status_str.argtypes = [ctypes.c_int]
+    lib.qkr_last_error.restype = ctypes.c_char_p
+    lib.qkr_last_error.argtypes = []
+    lib.qkr_version.restype = ctypes.c_int
+    lib.qkr_version.argtypes = []
+    return lib
+
+
+LIB = _load()
+
+
+def status_str(status: int) -> str:
+    return LIB.qkr_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise QknrError(status, where)
+
+
+# ------------------------------------------------------------------ helpers
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return QKR_BF16
+    if t.dtype == torch.float32:
+        return QKR_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t, name, dtype=None, numel=None):
+    """Device pointer of a contiguous CUDA/HIP tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def pool_desc(k_pool, num_q_heads: int) -> Pool:
+    """Pool descriptor for pools shaped [num_kv_heads, num_pages*64, 128]."""
+    if k_pool.dim() != 3 or k_pool.shape[1] % PAGE_SIZE != 0:
+        raise ValueError("pools must be [num_kv_heads, num_pages*64, head_dim]")
+    return Pool(num_q_heads, k_pool.shape[0], k_pool.shape[2], PAGE_SIZE,
+                k_pool.shape[1] // PAGE_SIZE, _dtype_code(k_pool), 0)
+
+
+# -------------------------------------------------------------- the C ABI
+
+def rope_table(theta: float, rope_rows: int, head_dim: int = HEAD_DIM):
+    """qkr_rope_table: float32 numpy (cos, sin), each [rope_rows, head_dim/2]."""
+    import numpy as np
+    cos = np.empty((rope_rows, head_dim // 2), dtype=np.float32)
+    sin = np.empty((rope_rows, head_dim // 2), dtype=np.float32)
+    _check(LIB.qkr_rope_table(float(theta), int(rope_rows), int(head_dim),
+                              cos.ctypes.data_as(ctypes.c_void_p), sin.ctypes.data_as(ctypes.c_void_p)),
+           "qkr_rope_table")
+    return cos, sin
+
+
+def qknorm_rope_append(q, k, v, q_gain, k_gain, rope_cos, rope_sin, positions, q_out, k_pool,
+                       v_pool, slots=None, table=None, eps: float = 1e-6, stream=None) -> None:
+    """QK-norm + RoPE of every token of q/k; q_out <- rotated q; k/v written into the pools.
+
+    The first ``len(slots)`` tokens write at ``slots``; the rest are decode rows
+    whose slot comes from ``table`` (row b = token index - len(slots)).
+    """
+    import torch
+    n = int(positions.numel())
+    n_q = q_out.shape[-1] // HEAD_DIM if q_out.dim() == 2 else 0
+    pool = pool_desc(k_pool, n_q)
+    n_slotted = 0 if slots is None else int(slots.numel())
+    ppr = 0 if table is None else int(table.shape[-1])
+    in_dt = _dtype_code(q)
+    st = LIB.qknorm_rope_append(
+        _stream(stream), ctypes.byref(pool), n,
+        _ptr(q, "q", q.dtype, n * n_q * HEAD_DIM), _ptr(k, "k", q.dtype, n * pool.num_kv_heads * HEAD_DIM),
+        _ptr(v, "v", q.dtype, n * pool.num_kv_heads * HEAD_DIM), in_dt,
+        _ptr(q_gain, "q_gain", torch.float32, HEAD_DIM), _ptr(k_gain, "k_gain", torch.float32, HEAD_DIM),
+        float(eps), _ptr(rope_cos, "rope_cos", torch.float32), _ptr(rope_sin, "rope_sin", torch.float32),
+        int(rope_cos.shape[0]), _ptr(positions, "positions", torch.int32),
+        _ptr(slots, "slots", torch.int32), n_slotted,
+        _ptr(table, "table", torch.int32, (n - n_slotted) * ppr), ppr,
+        _ptr(q_out, "q_out", k_pool.dtype, n * n_q * HEAD_DIM), _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype))
+    _check(st, "qknorm_rope_append")
+
+
+def decode_workspace_bytes(k_pool, num_q_heads: int, n_rows: int, pages_per_row: int) -> int:
+    pool = pool_desc(k_pool, num_q_heads)
+    return int(LIB.paged_decode_attn_workspace(ctypes.byref(pool), int(n_rows), int(pages_per_row)))
+
+
+def prefill_workspace_bytes(k_pool, num_q_heads: int, n_tokens: int) -> int:
+    pool = pool_desc(k_pool, num_q_heads)
+    return int(LIB.paged_prefill_attn_workspace(ctypes.byref(pool), int(n_tokens)))
+
+
+def paged_decode_attn(q, k_pool, v_pool, table, positions, scale: float, out, workspace=None,
+                      stream=None) -> None:
+    """out[b] <- attention of row b's query over positions 0..positions[b] of table[b]."""
+    import torch
+    n_q = q.shape[-1] // HEAD_DIM
+    pool = pool_desc(k_pool, n_q)
+    n_rows = int(positions.numel())
+    ppr = int(table.shape[-1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = LIB.paged_decode_attn(
+        _stream(stream), ctypes.byref(pool), n_rows, _ptr(q, "q", k_pool.dtype, n_rows * n_q * HEAD_DIM),
+        _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
+        _ptr(table, "table", torch.int32, n_rows * ppr), ppr, _ptr(positions, "positions", torch.int32),
+        float(scale), _ptr(out, "out", torch.float32, n_rows * n_q * HEAD_DIM),
+        _ptr(workspace, "workspace"), ws_bytes)
+    _check(st, "paged_decode_attn")
+
+
+def paged_prefill_attn(q, k_pool, v_pool, table, rows, positions, scale: float, out, workspace=None,
+                       stream=None) -> None:
+    """out[p] <- attention of token p over positions 0..positions[p] of table[rows[p]]."""
+    import torch
+    n_q = q.shape[-1] // HEAD_DIM
+    pool = pool_desc(k_pool, n_q)
+    n = int(positions.numel())
+    ppr = int(table.shape[-1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = LIB.paged_prefill_attn(
+        _stream(stream), ctypes.byref(pool), n, _ptr(q, "q", k_pool.dtype, n * n_q * HEAD_DIM),
+        _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
+        _ptr(table, "table", torch.int32), int(table.shape[0]), ppr,
+        _ptr(rows, "rows", torch.int32, n), _ptr(positions, "positions", torch.int32, n),
+        float(scale), _ptr(out, "out", torch.float32, n * n_q * HEAD_DIM),
+        _ptr(workspace, "workspace"), ws_bytes)
+    _check(st, "paged_prefill_attn")
+
+
+def version() -> int:
+    return int(LIB.qkr_version())
+
+
+def last_error() -> str:
+    return LIB.qkr_last_error().decode()

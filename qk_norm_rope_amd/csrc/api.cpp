@@ -1,0 +1,185 @@
+// Host side of the C ABI declared in include/qknr.h: argument checks, workspace
+// sizing, kernel selection and launches on the caller's stream.
+//
+// Every check runs before anything is enqueued (nest "models/qwen3-8b/files",
+// README: names, shapes and dtypes are checked before anything runs;
+// src/attention.linnet where-clause: Heads % KvHeads == 0, HeadDim even,
+// PageSize > 0).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdint>
+
+#include "../../include/qknr.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kHeadDimC = 128;
+constexpr int kPageSizeC = 64;
+
+
+int check_pool(const qkr_pool* pool) {
+  if (!pool) return QKR_EINVAL;
+  if (pool->num_q_heads <= 0 || pool->num_kv_heads <= 0 || pool->num_pages <= 0) return QKR_EINVAL;
+  if (pool->num_q_heads % pool->num_kv_heads != 0) return QKR_EINVAL;
+  if (pool->reserved != 0) return QKR_EINVAL;
+  if (pool->dtype != QKR_F32 && pool->dtype != QKR_BF16) return QKR_EUNSUPPORTED;
+  if (pool->head_dim != kHeadDimC || pool->page_size != kPageSizeC) return QKR_EUNSUPPORTED;
+  if (pool->num_q_heads / pool->num_kv_heads != 4) return QKR_EUNSUPPORTED;
+  // slot indices are formed in 64-bit; keep the element count of one pool addressable
+  if (pool->num_pages > (int64_t(1) << 40) / (64 * 128)) return QKR_EUNSUPPORTED;
+  return QKR_OK;
+}
+
+thread_local char g_last_error[256] = "";
+
+int launch_status(hipError_t e) {
+  if (e == hipSuccess) return QKR_OK;
+  snprintf(g_last_error, sizeof(g_last_error), "%s (hipError %d)", hipGetErrorString(e), (int)e);
+  return QKR_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qkr_version(void) { return 100; }
+
+const char* qkr_last_error(void) { return g_last_error; }
+
+const char* qkr_status_str(int s) {
+  switch (s) {
+    case QKR_OK: return "ok";
+    case QKR_EINVAL: return "invalid argument";
+    case QKR_EUNSUPPORTED: return "unsupported shape or dtype";
+    case QKR_EWORKSPACE: return "workspace missing or too small";
+    case QKR_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int qkr_rope_table(double theta, int32_t rope_rows, int32_t head_dim, float* cos_out, float* sin_out) {
+  if (!cos_out || !sin_out || rope_rows < 0 || head_dim <= 0 || head_dim % 2 != 0 || !(theta > 0.0))
+    return QKR_EINVAL;
+  const int half = head_dim / 2;
+  for (int i = 0; i < half; ++i) {
+    const double inv = 1.0 / std::pow(theta, (2.0 * i) / head_dim);
+    for (int32_t pos = 0; pos < rope_rows; ++pos) {
+      const double a = pos * inv;
+      cos_out[(int64_t)pos * half + i] = (float)std::cos(a);
+    }
+    for (int32_t pos = 0; pos < rope_rows; ++pos) {
+      const double a = pos * inv;
+      sin_out[(int64_t)pos * half + i] = (float)std::sin(a);
+    }
+  }
+  return QKR_OK;
+}
+
+int qknorm_rope_append(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                       const void* q, const void* k, const void* v, int32_t in_dtype,
+                       const float* q_gain, const float* k_gain, float eps,
+                       const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                       const int32_t* positions, const int32_t* slots, int32_t n_slotted,
+                       const int32_t* table, int32_t pages_per_row,
+                       void* q_out, void* k_pool, void* v_pool) {
+  int st = check_pool(pool);
+  if (st != QKR_OK) return st;
+  if (n_tokens < 0 || n_slotted < 0 || n_slotted > n_tokens) return QKR_EINVAL;
+  if (in_dtype != QKR_F32 && in_dtype != QKR_BF16) return QKR_EUNSUPPORTED;
+  if (n_tokens == 0) return QKR_OK;
+  if (!q || !k || !v || !q_gain || !k_gain || !rope_cos || !rope_sin || !positions || !q_out ||
+      !k_pool || !v_pool)
+    return QKR_EINVAL;
+  if (rope_rows <= 0) return QKR_EINVAL;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return QKR_EINVAL;
+  if (n_slotted > 0 && !slots) return QKR_EINVAL;
+  if (n_slotted < n_tokens && (!table || pages_per_row <= 0)) return QKR_EINVAL;
+  qknr::AppendArgs a;
+  a.n_tokens = n_tokens;
+  a.n_q_heads = pool->num_q_heads;
+  a.n_kv_heads = pool->num_kv_heads;
+  a.q = q; a.k = k; a.v = v;
+  a.in_bf16 = in_dtype == QKR_BF16;
+  a.out_bf16 = pool->dtype == QKR_BF16;
+  a.q_gain = q_gain; a.k_gain = k_gain; a.eps = eps;
+  a.rope_cos = rope_cos; a.rope_sin = rope_sin; a.rope_rows = rope_rows;
+  a.positions = positions; a.slots = slots; a.n_slotted = n_slotted;
+  a.table = table; a.pages_per_row = pages_per_row; a.num_pages = pool->num_pages;
+  a.q_out = q_out; a.k_pool = k_pool; a.v_pool = v_pool;
+  return launch_status(qknr::launch_append(static_cast<hipStream_t>(stream), a));
+}
+
+size_t paged_decode_attn_workspace(const qkr_pool* pool, int32_t n_rows, int32_t pages_per_row) {
+  if (check_pool(pool) != QKR_OK || n_rows <= 0 || pages_per_row <= 0) return 0;
+  if (pool->dtype != QKR_BF16) return 0;
+  return qknr::decode_workspace_bytes(n_rows, pool->num_kv_heads, pages_per_row);
+}
+
+int paged_decode_attn(void* stream, const qkr_pool* pool, int32_t n_rows,
+                      const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* table, int32_t pages_per_row,
+                      const int32_t* positions, float scale, float* out,
+                      void* workspace, size_t workspace_bytes) {
+  int st = check_pool(pool);
+  if (st != QKR_OK) return st;
+  if (n_rows < 0) return QKR_EINVAL;
+  if (n_rows == 0) return QKR_OK;
+  if (!q || !k_pool || !v_pool || !table || !positions || !out || pages_per_row <= 0) return QKR_EINVAL;
+  if (!std::isfinite(scale)) return QKR_EINVAL;
+  qknr::AttnArgs a;
+  a.n_queries = n_rows;
+  a.n_q_heads = pool->num_q_heads;
+  a.n_kv_heads = pool->num_kv_heads;
+  a.bf16 = pool->dtype == QKR_BF16;
+  a.q = q; a.k_pool = k_pool; a.v_pool = v_pool;
+  a.num_pages = pool->num_pages;
+  a.table = table; a.n_table_rows = n_rows; a.pages_per_row = pages_per_row;
+  a.rows = nullptr; a.positions = positions; a.scale = scale; a.out = out;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!a.bf16) return launch_status(qknr::launch_attention_generic(s, a));
+  const size_t need = qknr::decode_workspace_bytes(n_rows, pool->num_kv_heads, pages_per_row);
+  if (!workspace || workspace_bytes < need) return QKR_EWORKSPACE;
+  return launch_status(qknr::launch_decode_bf16(s, a));
+}
+
+size_t paged_prefill_attn_workspace(const qkr_pool* pool, int32_t n_tokens) {
+  if (check_pool(pool) != QKR_OK || n_tokens <= 0) return 0;
+  if (pool->dtype != QKR_BF16) return 0;
+  return qknr::prefill_workspace_bytes(n_tokens, pool->num_kv_heads);
+}
+
+int paged_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                       const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
+                       const int32_t* rows, const int32_t* positions,
+                       float scale, float* out, void* workspace, size_t workspace_bytes) {
+  int st = check_pool(pool);
+  if (st != QKR_OK) return st;
+  if (n_tokens < 0) return QKR_EINVAL;
+  if (n_tokens == 0) return QKR_OK;
+  if (!q || !k_pool || !v_pool || !table || !rows || !positions || !out || n_table_rows <= 0 ||
+      pages_per_row <= 0)
+    return QKR_EINVAL;
+  if (!std::isfinite(scale)) return QKR_EINVAL;
+  qknr::AttnArgs a;
+  a.n_queries = n_tokens;
+  a.n_q_heads = pool->num_q_heads;
+  a.n_kv_heads = pool->num_kv_heads;
+  a.bf16 = pool->dtype == QKR_BF16;
+  a.q = q; a.k_pool = k_pool; a.v_pool = v_pool;
+  a.num_pages = pool->num_pages;
+  a.table = table; a.n_table_rows = n_table_rows; a.pages_per_row = pages_per_row;
+  a.rows = rows; a.positions = positions; a.scale = scale; a.out = out;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!a.bf16) return launch_status(qknr::launch_attention_generic(s, a));
+  const size_t need = qknr::prefill_workspace_bytes(n_tokens, pool->num_kv_heads);
+  if (!workspace || workspace_bytes < need) return QKR_EWORKSPACE;
+  return launch_status(qknr::launch_prefill_bf16(s, a));
+}
+
+}  // extern "C"

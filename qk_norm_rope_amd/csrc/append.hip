@@ -1,0 +1,171 @@
+// K1: fused QK-norm + RoPE + paged cache append.
+//
+// nest "models/qwen3-8b/files": README (QK-norm: RMS normalisation of every head's
+// head_dim slice, after the split into heads and before rope; eps 1e-6),
+// src/attention.linnet (decode_paged / prefill_paged / step_paged: q and k are
+// normed and rotated, then k and v are written into the pool at the token's slot),
+// src/norm.linnet, src/rope.linnet. fantasma "src/inference/model.zig":
+// fullAttentionForward and applyRope (rotate_half pairing of i with i + 64).
+//
+// One workgroup per token; 16 lanes per head vector, lane j holding elements
+// 4j..4j+3 of each half. The float32 arithmetic is fixed (no contraction into
+// fused multiply-adds, pairwise sums in a fixed tree, correctly rounded sqrt and
+// division) so the stored bytes are reproducible bit for bit:
+//   p_i  = x_i*x_i + x_{i+64}*x_{i+64}                      (i < 64)
+//   ss   = pairwise tree over i (neighbours first)
+//   r    = 1 / sqrt(ss/128 + eps)
+//   y_d  = (x_d * r) * g_d
+//   y'_i = y_i*c_i - y_{i+64}*s_i,  y'_{i+64} = y_{i+64}*c_i + y_i*s_i
+// The stored value rounds to the pool dtype (bfloat16: nearest even).
+#include "common.h"
+#include "kernels.h"
+
+#pragma clang fp contract(off)
+
+namespace qknr {
+namespace {
+
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+  __device__ static void load(const float* p, float (&o)[4]) {
+    float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+  __device__ static void store(float* p, const float (&o)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+};
+template <> struct Vec4<uint16_t> {
+  __device__ static void load(const uint16_t* p, float (&o)[4]) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+  }
+  __device__ static void store(uint16_t* p, const float (&o)[4]) {
+    uint2 v;
+    v.x = f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16);
+    v.y = f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = v;
+  }
+};
+
+template <typename TIn, typename TOut>
+__global__ __launch_bounds__(256) void qknorm_rope_append_kernel(
+    int n_q_heads, int n_kv_heads,
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const float* __restrict__ q_gain, const float* __restrict__ k_gain, float eps,
+    const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rope_rows,
+    const int* __restrict__ positions, const int* __restrict__ slots, int n_slotted,
+    const int* __restrict__ table, int pages_per_row, int64_t num_pages,
+    TOut* __restrict__ q_out, TOut* __restrict__ k_pool, TOut* __restrict__ v_pool) {
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int pos = positions[t];
+  if (pos < 0 || pos >= rope_rows) return;  // no rotation exists for it: skip the token
+
+  const int64_t pool_slots = num_pages * kPageSize;
+  int64_t slot = -1;
+  if (t < n_slotted) {
+    slot = slots[t];
+  } else {
+    const int b = t - n_slotted;
+    const int pg = pos / kPageSize;
+    if (pg < pages_per_row) {
+      const int64_t page = table[(int64_t)b * pages_per_row + pg];
+      if (page >= 0 && page < num_pages) slot = page * kPageSize + pos % kPageSize;
+    }
+  }
+  if (slot >= pool_slots) slot = -1;
+
+  const int j = tid & 15;
+  const float* cs = rope_cos + (int64_t)pos * (kHeadDim / 2) + 4 * j;
+  const float* sn = rope_sin + (int64_t)pos * (kHeadDim / 2) + 4 * j;
+  float c[4], s[4];
+  Vec4<float>::load(cs, c);
+  Vec4<float>::load(sn, s);
+
+  const int n_norm = n_q_heads + n_kv_heads;
+  for (int hv = tid >> 4; hv < n_norm; hv += 16) {
+    const TIn* src;
+    const float* g;
+    TOut* dst;
+    bool write = true;
+    if (hv < n_q_heads) {
+      src = q + ((int64_t)t * n_q_heads + hv) * kHeadDim;
+      g = q_gain;
+      dst = q_out + ((int64_t)t * n_q_heads + hv) * kHeadDim;
+    } else {
+      const int kh = hv - n_q_heads;
+      src = k + ((int64_t)t * n_kv_heads + kh) * kHeadDim;
+      g = k_gain;
+      write = slot >= 0;
+      dst = k_pool + ((int64_t)kh * pool_slots + (write ? slot : 0)) * kHeadDim;
+    }
+    float a[4], b[4];
+    Vec4<TIn>::load(src + 4 * j, a);
+    Vec4<TIn>::load(src + kHeadDim / 2 + 4 * j, b);
+
+    float p0 = a[0] * a[0] + b[0] * b[0];
+    float p1 = a[1] * a[1] + b[1] * b[1];
+    float p2 = a[2] * a[2] + b[2] * b[2];
+    float p3 = a[3] * a[3] + b[3] * b[3];
+    float ss = (p0 + p1) + (p2 + p3);
+    ss = ss + __shfl_xor(ss, 1, 16);
+    ss = ss + __shfl_xor(ss, 2, 16);
+    ss = ss + __shfl_xor(ss, 4, 16);
+    ss = ss + __shfl_xor(ss, 8, 16);
+    const float ms = ss * (1.0f / kHeadDim);
+    const float r = 1.0f / __builtin_sqrtf(ms + eps);
+
+    float ga[4], gb[4];
+    Vec4<float>::load(g + 4 * j, ga);
+    Vec4<float>::load(g + kHeadDim / 2 + 4 * j, gb);
+    float oa[4], ob[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ya = (a[i] * r) * ga[i];
+      const float yb = (b[i] * r) * gb[i];
+      const float ac = ya * c[i];
+      const float bs = yb * s[i];
+      const float bc = yb * c[i];
+      const float as = ya * s[i];
+      oa[i] = ac - bs;
+      ob[i] = bc + as;
+    }
+    if (write) {
+      Vec4<TOut>::store(dst + 4 * j, oa);
+      Vec4<TOut>::store(dst + kHeadDim / 2 + 4 * j, ob);
+    }
+  }
+
+  if (slot >= 0) {
+    // v: cast only, 4 elements per thread per pass
+    for (int e = tid; e < n_kv_heads * (kHeadDim / 4); e += 256) {
+      const int kh = e / (kHeadDim / 4);
+      const int c4 = e % (kHeadDim / 4);
+      float x[4];
+      Vec4<TIn>::load(v + ((int64_t)t * n_kv_heads + kh) * kHeadDim + 4 * c4, x);
+      Vec4<TOut>::store(v_pool + ((int64_t)kh * pool_slots + slot) * kHeadDim + 4 * c4, x);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(hipStream_t stream, const AppendArgs& a) {
+  const dim3 grid(a.n_tokens), block(256);
+#define QKNR_APPEND(TI, TO)                                                            \
+  hipLaunchKernelGGL((qknorm_rope_append_kernel<TI, TO>), grid, block, 0, stream,       \
+                     a.n_q_heads, a.n_kv_heads, (const TI*)a.q, (const TI*)a.k,         \
+                     (const TI*)a.v, a.q_gain, a.k_gain, a.eps, a.rope_cos, a.rope_sin, \
+                     a.rope_rows, a.positions, a.slots, a.n_slotted, a.table,           \
+                     a.pages_per_row, a.num_pages, (TO*)a.q_out, (TO*)a.k_pool,         \
+                     (TO*)a.v_pool)
+  if (a.in_bf16 && a.out_bf16) QKNR_APPEND(uint16_t, uint16_t);
+  else if (a.in_bf16) QKNR_APPEND(uint16_t, float);
+  else if (a.out_bf16) QKNR_APPEND(float, uint16_t);
+  else QKNR_APPEND(float, float);
+#undef QKNR_APPEND
+  return hipGetLastError();
+}
+
+}  // namespace qknr

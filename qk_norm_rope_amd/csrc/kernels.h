@@ -1,0 +1,56 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qknr {
+
+struct AppendArgs {
+  int n_tokens, n_q_heads, n_kv_heads;
+  const void *q, *k, *v;
+  bool in_bf16, out_bf16;
+  const float *q_gain, *k_gain;
+  float eps;
+  const float *rope_cos, *rope_sin;
+  int rope_rows;
+  const int32_t *positions, *slots;
+  int n_slotted;
+  const int32_t* table;
+  int pages_per_row;
+  int64_t num_pages;
+  void *q_out, *k_pool, *v_pool;
+};
+
+struct AttnArgs {
+  int n_queries;          // decode rows, or prefill tokens
+  int n_q_heads, n_kv_heads;
+  bool bf16;              // pool / q dtype
+  const void* q;
+  const void *k_pool, *v_pool;
+  int64_t num_pages;
+  const int32_t* table;
+  int n_table_rows, pages_per_row;
+  const int32_t* rows;    // prefill: row of each token; decode: nullptr (row = index)
+  const int32_t* positions;
+  float scale;
+  float* out;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+hipError_t launch_append(hipStream_t stream, const AppendArgs& a);
+
+// Decode: split-K over page ranges with a fused last-arriver merge.
+size_t decode_workspace_bytes(int n_rows, int n_kv_heads, int pages_per_row);
+hipError_t launch_decode_bf16(hipStream_t stream, const AttnArgs& a);
+
+// Prefill: MFMA flash attention over 64-token tiles of the pack.
+size_t prefill_workspace_bytes(int n_tokens, int n_kv_heads);
+hipError_t launch_prefill_bf16(hipStream_t stream, const AttnArgs& a);
+
+// One workgroup per (query, KV head); any pool dtype. Used for float32 pools.
+hipError_t launch_attention_generic(hipStream_t stream, const AttnArgs& a);
+
+}  // namespace qknr

@@ -1,0 +1,152 @@
+"""Shared helpers of the GPU parity tests: run a workload through the library
+(through its C ABI binding) and build the oracle's view of the same pool."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+import workloads as W
+
+DEV = "cuda"
+TOL_F32 = 1e-4   # max abs error, float32 pool
+TOL_BF16 = 2e-2  # max abs error, bfloat16 K/V with float32 accumulation
+
+_ROPE = {}
+
+
+def lib():
+    import qk_norm_rope_amd as Q
+    return Q
+
+
+def rope_tables():
+    if "t" not in _ROPE:
+        cos, sin = lib().rope_table(O.ROPE_THETA, W.MAX_POSITIONS, W.HEAD_DIM)
+        _ROPE["t"] = (torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV))
+    return _ROPE["t"]
+
+
+def bits(t: torch.Tensor) -> torch.Tensor:
+    """Integer view of a float tensor, for bitwise comparisons (NaN == NaN)."""
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def host_values(t: torch.Tensor, dtype: str) -> np.ndarray:
+    """Device tensor -> the oracle's representation (float32, or bf16 bits)."""
+    if dtype == "bf16":
+        return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.detach().cpu().numpy()
+
+
+class OraclePool:
+    """The oracle's view of one pool (K: which=0, V: which=1).
+
+    ``pool[g, slots]`` returns the stored values at ``slots`` of KV head g: the
+    pre-step history regenerated on the host from the seeded generator, then the
+    oracle's own writes of the step (``pool[:, s, :] = rows``). Nothing comes
+    from the GPU.
+    """
+
+    def __init__(self, w: W.Workload, which: int):
+        self.w = w
+        self.which = which
+        self.writes = {}
+
+    def __setitem__(self, key, rows):
+        _, s, _ = key
+        self.writes[int(s)] = np.array(rows)
+
+    def __getitem__(self, key):
+        g, slots = key
+        slots = np.asarray(slots, dtype=np.int64)
+        vals = W.host_history(self.w, self.which, g, slots)
+        if self.writes:
+            for i, s in enumerate(slots):
+                r = self.writes.get(int(s))
+                if r is not None:
+                    vals[i] = r[g]
+        return vals
+
+
+class Run:
+    """One workload on the GPU: inputs, pre-step pools, and the library's outputs."""
+
+    def __init__(self, w: W.Workload, keep_pre: bool = True):
+        self.w = w
+        self.t = W.upload(w, DEV)
+        self.k_pool, self.v_pool = W.make_pools(w, DEV)
+        self.k_pre = self.k_pool.clone() if keep_pre else None
+        self.v_pre = self.v_pool.clone() if keep_pre else None
+        self.td = W.torch_dtype(w.dtype)
+        self.q_out = None
+        self.pre_out = None
+        self.dec_out = None
+
+    def positions_all(self):
+        return torch.cat([self.t["positions"], self.t["step_positions"]])
+
+    def append(self):
+        Q = lib()
+        w, t = self.w, self.t
+        cos, sin = rope_tables()
+        self.q_out = torch.empty((w.n_tokens, W.NUM_Q_HEADS * W.HEAD_DIM), dtype=self.td, device=DEV)
+        Q.qknorm_rope_append(t["q"], t["k"], t["v"], t["q_gain"], t["k_gain"], cos, sin,
+                             self.positions_all(), self.q_out, self.k_pool, self.v_pool,
+                             slots=t["slots"] if w.n_prefill else None,
+                             table=t["decode_table"] if w.n_decode else None)
+
+    def prefill(self):
+        Q = lib()
+        w, t = self.w, self.t
+        P = w.n_prefill
+        self.pre_out = torch.empty((P, W.NUM_Q_HEADS * W.HEAD_DIM), dtype=torch.float32, device=DEV)
+        ws = torch.zeros(max(1, Q.prefill_workspace_bytes(self.k_pool, W.NUM_Q_HEADS, P)),
+                         dtype=torch.uint8, device=DEV)
+        Q.paged_prefill_attn(self.q_out[:P], self.k_pool, self.v_pool, t["table"], t["rows"],
+                             t["positions"], W.SCALE, self.pre_out, ws)
+
+    def decode(self, workspace=None):
+        Q = lib()
+        w, t = self.w, self.t
+        P, R = w.n_prefill, w.n_decode
+        self.dec_out = torch.empty((R, W.NUM_Q_HEADS * W.HEAD_DIM), dtype=torch.float32, device=DEV)
+        if workspace is None:
+            workspace = decode_workspace(self.k_pool, R, w.pages_per_row)
+        Q.paged_decode_attn(self.q_out[P:], self.k_pool, self.v_pool, t["decode_table"],
+                            t["step_positions"], W.SCALE, self.dec_out, workspace)
+
+    def step(self):
+        self.append()
+        if self.w.n_prefill:
+            self.prefill()
+        if self.w.n_decode:
+            self.decode()
+        torch.cuda.synchronize()
+
+
+def decode_workspace(k_pool, n_rows, pages_per_row):
+    Q = lib()
+    n = Q.decode_workspace_bytes(k_pool, W.NUM_Q_HEADS, n_rows, pages_per_row)
+    return torch.zeros(max(1, n), dtype=torch.uint8, device=DEV)
+
+
+def oracle_append(w: W.Workload):
+    """Oracle q_out and stored k/v rows for every token of the step, and their slots."""
+    every_at = np.concatenate([w.positions, w.step_positions]).astype(np.int64)
+    dec_slots = [O.page_slot(w.decode_table[b], int(w.step_positions[b])) for b in range(w.n_decode)]
+    every_slot = np.concatenate([w.slots.astype(np.int64), np.asarray(dec_slots, dtype=np.int64)])
+    q_out, k_rows, v_rows = O.append(w.q, w.k, w.v, w.dtype, w.dtype, w.q_gain, w.k_gain, every_at)
+    return q_out, k_rows, v_rows, every_slot
+
+
+def oracle_pools(w: W.Workload, k_rows, v_rows, every_slot):
+    kp, vp = OraclePool(w, 0), OraclePool(w, 1)
+    O.apply_writes(kp, vp, every_slot, k_rows, v_rows)
+    return kp, vp
+
+
+def max_abs_err(got: np.ndarray, ref: np.ndarray) -> float:
+    assert got.shape == ref.shape
+    assert np.isfinite(got).all(), "non-finite output"
+    return float(np.max(np.abs(got.astype(np.float64) - ref)))

@@ -1,0 +1,125 @@
+"""The C ABI loads, exports what include/qknr.h declares, and rejects bad
+arguments on the host before anything is enqueued (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import qk_norm_rope_amd as Q
+from qk_norm_rope_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "qknr.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert set(_declared_functions()) == set(L.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert Q.status_str(0) == "ok"
+    assert "invalid" in Q.status_str(-1)
+    assert "workspace" in Q.status_str(-3)
+
+
+def test_rope_table_matches_oracle_bitwise():
+    # the library's host helper and the oracle compute the table independently
+    cos, sin = Q.rope_table(1e6, 40960, 128)
+    ocos, osin = O.rope_table(1e6, 40960, 128)
+    assert np.array_equal(cos, ocos)
+    assert np.array_equal(sin, osin)
+
+
+def _pool(**kw):
+    p = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64, num_pages=16,
+             dtype=L.QKR_BF16, reserved=0)
+    p.update(kw)
+    return L.Pool(**p)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
+
+
+def _append(pool, n=1, **kw):
+    args = dict(stream=None, n=n, q=FAKE, k=FAKE, v=FAKE, in_dtype=L.QKR_BF16, qg=FAKE, kg=FAKE,
+                eps=1e-6, cos=FAKE, sin=FAKE, rope_rows=100, pos=FAKE, slots=FAKE, n_slotted=n,
+                table=None, ppr=0, q_out=FAKE, kp=FAKE, vp=FAKE)
+    args.update(kw)
+    return L.LIB.qknorm_rope_append(args["stream"], ctypes.byref(pool), args["n"], args["q"], args["k"],
+                                    args["v"], args["in_dtype"], args["qg"], args["kg"], args["eps"],
+                                    args["cos"], args["sin"], args["rope_rows"], args["pos"],
+                                    args["slots"], args["n_slotted"], args["table"], args["ppr"],
+                                    args["q_out"], args["kp"], args["vp"])
+
+
+def test_append_host_checks():
+    assert _append(_pool(head_dim=64)) == -2
+    assert _append(_pool(page_size=32)) == -2
+    assert _append(_pool(num_q_heads=30)) == -1          # not a multiple of kv heads
+    assert _append(_pool(num_q_heads=16)) == -2          # group of 2 is not built
+    assert _append(_pool(reserved=1)) == -1
+    assert _append(_pool(), in_dtype=7) == -2
+    assert _append(_pool(), q=None) == -1
+    assert _append(_pool(), n=-1) == -1
+    assert _append(_pool(), n_slotted=2) == -1           # more slotted tokens than tokens
+    assert _append(_pool(), n=2, n_slotted=1) == -1      # decode tokens need a table
+    assert _append(_pool(), rope_rows=0) == -1
+    assert _append(_pool(), eps=float("nan")) == -1
+    assert _append(_pool(), n=0, q=None) == 0            # empty batch is a no-op
+
+
+def test_decode_and_prefill_host_checks():
+    pool = _pool()
+    lib = L.LIB
+    assert lib.paged_decode_attn(None, ctypes.byref(pool), 0, None, None, None, None, 0, None,
+                                 0.1, None, None, 0) == 0
+    assert lib.paged_decode_attn(None, ctypes.byref(pool), 2, FAKE, FAKE, FAKE, None, 4, FAKE,
+                                 0.1, FAKE, FAKE, 1 << 20) == -1
+    need = lib.paged_decode_attn_workspace(ctypes.byref(pool), 2, 4)
+    assert need > 0
+    assert lib.paged_decode_attn(None, ctypes.byref(pool), 2, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+                                 0.1, FAKE, FAKE, need - 1) == -3
+    assert lib.paged_decode_attn(None, ctypes.byref(pool), 2, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+                                 0.1, FAKE, None, need) == -3
+    assert lib.paged_decode_attn(None, ctypes.byref(pool), 2, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+                                 float("inf"), FAKE, FAKE, need) == -1
+    pneed = lib.paged_prefill_attn_workspace(ctypes.byref(pool), 100)
+    assert pneed >= 2 * 4
+    assert lib.paged_prefill_attn(None, ctypes.byref(pool), 100, FAKE, FAKE, FAKE, FAKE, 3, 4, None,
+                                  FAKE, 0.1, FAKE, FAKE, pneed) == -1
+    assert lib.paged_prefill_attn(None, ctypes.byref(pool), 100, FAKE, FAKE, FAKE, FAKE, 3, 4, FAKE,
+                                  FAKE, 0.1, FAKE, FAKE, pneed - 1) == -3
+    assert lib.paged_prefill_attn(None, ctypes.byref(_pool(head_dim=256)), 100, FAKE, FAKE, FAKE,
+                                  FAKE, 3, 4, FAKE, FAKE, 0.1, FAKE, FAKE, pneed) == -2
+
+
+def test_workspace_sizes_grow_with_work():
+    pool = _pool()
+    a = L.LIB.paged_decode_attn_workspace(ctypes.byref(pool), 8, 65)
+    b = L.LIB.paged_decode_attn_workspace(ctypes.byref(pool), 64, 640)
+    assert 0 < a < b
+    assert L.LIB.paged_decode_attn_workspace(ctypes.byref(_pool(dtype=L.QKR_F32)), 8, 65) == 0
+    assert L.LIB.paged_prefill_attn_workspace(ctypes.byref(pool), 4096) >= 64 * 4
+
+
+def test_rope_table_rejects_bad_arguments():
+    buf = np.zeros(4, np.float32)
+    p = buf.ctypes.data_as(ctypes.c_void_p)
+    assert L.LIB.qkr_rope_table(1e6, 1, 3, p, p) == -1
+    assert L.LIB.qkr_rope_table(-1.0, 1, 8, p, p) == -1
+    assert L.LIB.qkr_rope_table(1e6, 1, 8, None, p) == -1

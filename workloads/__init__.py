@@ -66,6 +66,7 @@ class Workload:
     k_gain: np.ndarray             # float32 [128]
     history: list = field(default_factory=list)   # (row, n) : positions 0..n-1 pre-filled
     row_pages: dict = field(default_factory=dict)  # row -> allocated page ids, in order
+    _history_slots: np.ndarray = field(default=None, repr=False)
 
     @property
     def n_prefill(self) -> int:
@@ -94,11 +95,12 @@ class Workload:
         return expanded[:n]
 
     def history_slots(self) -> np.ndarray:
-        """Every slot that holds a pre-step value (shared prefix pages once)."""
-        s = [self.row_slot_list(r, n) for r, n in self.history if n > 0]
-        if not s:
-            return np.zeros(0, dtype=np.int64)
-        return np.unique(np.concatenate(s))
+        """Every slot that holds a pre-step value (shared prefix pages once), sorted."""
+        if self._history_slots is None:
+            s = [self.row_slot_list(r, n) for r, n in self.history if n > 0]
+            self._history_slots = (np.unique(np.concatenate(s)) if s
+                                   else np.zeros(0, dtype=np.int64))
+        return self._history_slots
 
 
 def _bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -259,7 +261,9 @@ def host_history(w: Workload, which: int, kv_head: int, slots) -> np.ndarray:
     import torch
     slots = np.asarray(slots, dtype=np.int64)
     hs = w.history_slots()
-    present = np.isin(slots, hs)
+    pos = np.searchsorted(hs, slots)
+    present = (pos < len(hs)) & (hs[np.minimum(pos, max(len(hs) - 1, 0))] == slots) if len(hs) else \
+        np.zeros(len(slots), dtype=bool)
     vals = history_values(w.seed, which, kv_head, slots)
     vals[torch.as_tensor(~present)] = float("nan")
     t = vals.to(torch_dtype(w.dtype))
