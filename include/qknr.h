@@ -133,6 +133,7 @@ int qknorm_rope_append(void* stream, const qkr_pool* pool, int32_t n_tokens,
  * the split depends only on positions, so the result does not depend on where
  * the pages sit in the pool.
  *
+ * A bfloat16 pool takes at most 12288 rows per call (QKR_EUNSUPPORTED above).
  * workspace: device memory of at least paged_decode_attn_workspace() bytes. It
  * must be zero-filled before its first use; every call leaves it ready for the
  * next (its counters return to zero). Calls that share a workspace must be

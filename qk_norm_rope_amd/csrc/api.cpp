@@ -141,6 +141,7 @@ int paged_decode_attn(void* stream, const qkr_pool* pool, int32_t n_rows,
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!a.bf16) return launch_status(qknr::launch_attention_generic(s, a));
+  if (n_rows > qknr::decode_max_rows()) return QKR_EUNSUPPORTED;
   const size_t need = qknr::decode_workspace_bytes(n_rows, pool->num_kv_heads, pages_per_row);
   if (!workspace || workspace_bytes < need) return QKR_EWORKSPACE;
   return launch_status(qknr::launch_decode_bf16(s, a));

@@ -1,4 +1,5 @@
-// K2: paged decode attention, split over page ranges (flash decoding), bfloat16.
+// K2: paged decode attention, bfloat16, split evenly over the GPU (stream-K
+// flash decoding).
 //
 // nest "models/qwen3-8b/files": Entries table (decode_paged: row b's positions lie
 // in the pages table[b] lists, pages of 64) and src/attention.linnet (decode_paged
@@ -7,117 +8,172 @@
 // fullAttentionForward: query head h reads KV head h / 4; scores scaled by
 // 1/sqrt(head_dim); max-subtracted softmax; weighted sum of V.
 //
-// Work item = (row b, KV head g, range of the row's pages). One workgroup of 4
-// waves runs an item; wave w takes keys 16w..16w+15 of every page, so each 16 KB
-// K chunk and 16 KB V chunk of a (page, KV head) is read once for all 4 query
-// heads of the group:
-//   * scores of the 4 heads x 16 keys on one v_mfma_f32_16x16x32_bf16 chain
-//     (query rows 4..15 are zero);
-//   * an online softmax per head with wave-level max/sum reductions;
-//   * P.V on the vector ALU, lane l holding 8 dimensions of 4 keys.
-// The 4 waves merge through LDS; when a row has several items, each writes its
-// (max, sum, acc) state to the workspace and the last one to finish (a ticket
-// counter per (row, KV head)) merges them in split order, so the result does not
-// depend on timing. The split size depends only on the positions.
+// Work list: unit = (row b, KV head g, page p of the row), ordered by row, then KV
+// head, then page; a "segment" is the run of units of one (b, g). The grid is the
+// number of workgroups the GPU holds at once, and workgroup i takes units
+// [i*U/G, (i+1)*U/G): every workgroup streams the same number of 32 KB K/V page
+// chunks, whatever the rows' lengths. A segment that lies inside one workgroup's
+// range is finished there; a segment cut by range ends yields one partial
+// softmax state (max, sum, acc) per workgroup touching it, and the last of them
+// to finish (ticket counter per segment) merges them in workgroup order, so the
+// result depends only on the positions, never on timing or on where pages sit.
 //
-// Every workgroup plans the same split from the positions (sum and max of the
-// rows' page counts), then walks the item list with a grid stride.
+// Inside a workgroup, wave w takes keys 16w..16w+15 of each page, so each page's
+// K and V are read once for the 4 query heads of the group:
+//   * scores of 4 heads x 16 keys: 4 x v_mfma_f32_16x16x32_bf16 (query rows 4..15
+//     are zero);
+//   * online softmax per head, row max by DPP rotations inside 16-lane rows;
+//   * P.V on the vector ALU, lane l holding 8 dimensions of 4 keys, the
+//     probabilities passed through LDS;
+//   * the next page's K/V loads are in flight while the current page computes.
+// Partial states travel through agent-coherent (sc1) stores and loads with an
+// explicit wait before the ticket, so no cache-wide write-back is needed.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace qknr {
 namespace {
 
-constexpr int kMaxSplits = 64;        // items per (row, KV head) at most
-constexpr int kMinSplitPages = 2;     // pages per item at least
-constexpr int kTargetItems = 2048;    // items the plan aims for
-constexpr int kGridCap = 2048;        // workgroups launched at most
-constexpr int kPartial = kGroup * (kHeadDim + 2);  // floats per item: per head (m, l, acc[128])
+constexpr int kPartial = kGroup * (kHeadDim + 2);  // floats per partial: per head (m, l, acc[128])
+constexpr int kMaxGrid = 2048;                     // workgroups launched at most
+constexpr int kMaxRows = 12288;                    // rows per call (LDS prefix table)
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
-}
-__device__ __forceinline__ int wave_max_i(int x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = max(x, __shfl_xor(x, m));
-  return x;
-}
-__device__ __forceinline__ float max16(float x) {
-  x = fmaxf(x, __shfl_xor(x, 8, 16));
-  x = fmaxf(x, __shfl_xor(x, 4, 16));
-  x = fmaxf(x, __shfl_xor(x, 2, 16));
-  x = fmaxf(x, __shfl_xor(x, 1, 16));
-  return x;
-}
-__device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 8, 16);
-  x += __shfl_xor(x, 4, 16);
-  x += __shfl_xor(x, 2, 16);
-  x += __shfl_xor(x, 1, 16);
+struct DecodeParams {
+  int n_rows, n_kv;
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  int64_t num_pages;
+  const int* table;
+  int pages_per_row;
+  const int* positions;
+  float scale_log2;
+  float* out;
+  int* counters;      // [n_rows * n_kv], zero between calls
+  float* partials;    // [grid][2][kPartial]
+};
+
+// max over the 16 lanes of a DPP row, result in every lane of the row
+__device__ __forceinline__ float row_max16(float x) {
+#define QKNR_ROR(v, n) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + (n), 0xf, 0xf, false))
+  x = fmaxf(x, QKNR_ROR(x, 8));
+  x = fmaxf(x, QKNR_ROR(x, 4));
+  x = fmaxf(x, QKNR_ROR(x, 2));
+  x = fmaxf(x, QKNR_ROR(x, 1));
+#undef QKNR_ROR
   return x;
 }
 
-__global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
-    int n_rows, int n_kv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
-    const uint16_t* __restrict__ v_pool, int64_t num_pages, const int* __restrict__ table,
-    int pages_per_row, const int* __restrict__ positions, float scale_log2, float* __restrict__ out,
-    int* __restrict__ counters, float* __restrict__ partials) {
-  __shared__ int s_red[8];
-  __shared__ int s_last;
+__device__ __forceinline__ void store_sc1(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_sc1(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ long long range_begin(int i, long long U, int G) { return (long long)i * U / G; }
+
+// workgroup whose range holds unit u
+__device__ __forceinline__ int owner(long long u, long long U, int G) {
+  int i = (int)((u * G) / U);
+  while (i + 1 < G && range_begin(i + 1, U, G) <= u) ++i;
+  while (i > 0 && range_begin(i, U, G) > u) --i;
+  return i;
+}
+
+struct PageRegs {
+  bf16x8 k[4];
+  uint4 v[4];
+  bool ok;
+};
+
+__global__ __launch_bounds__(256) void paged_decode_bf16_kernel(DecodeParams P) {
+  extern __shared__ int s_prefix[];   // [n_rows + 1]: units before row b
+  __shared__ __attribute__((aligned(16))) float s_p[4][16][kGroup];
   __shared__ float s_m[4][kGroup], s_l[4][kGroup];
   __shared__ __attribute__((aligned(16))) float s_acc[4][kGroup][kHeadDim];
+  __shared__ int s_scan[4];
+  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int l = tid & 63;
   const int hr = l & 15;   // MFMA row/column index within a 16-lane group
-  const int G = l >> 4;    // 16-lane group
-  const int n_q = n_kv * kGroup;
-  const int max_pos = pages_per_row * kPageSize;
+  const int G4 = l >> 4;   // 16-lane group
+  const int n_q = P.n_kv * kGroup;
+  const int max_pos = P.pages_per_row * kPageSize;
+  const int n_rows = P.n_rows;
 
-  // ---- plan: the same in every workgroup
-  int sum = 0, mx = 0;
-  for (int b = tid; b < n_rows; b += 256) {
-    const int p = positions[b];
-    const int np = (p >= 0 && p < max_pos) ? p / kPageSize + 1 : 0;
-    sum += np;
-    mx = max(mx, np);
+  // ---- units per row, exclusive prefix over rows (blocked scan)
+  {
+    const int per = (n_rows + 255) / 256;
+    const int b0 = tid * per;
+    int local = 0;
+    for (int b = b0; b < min(b0 + per, n_rows); ++b) {
+      const int p = P.positions[b];
+      local += (p >= 0 && p < max_pos) ? (p / kPageSize + 1) * P.n_kv : 0;
+    }
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (l >= d) incl += y;
+    }
+    if (l == 63) s_scan[w] = incl;
+    __syncthreads();
+    int off = 0;
+    for (int ww = 0; ww < w; ++ww) off += s_scan[ww];
+    int run = off + incl - local;
+    for (int b = b0; b < min(b0 + per, n_rows); ++b) {
+      s_prefix[b] = run;
+      const int p = P.positions[b];
+      run += (p >= 0 && p < max_pos) ? (p / kPageSize + 1) * P.n_kv : 0;
+    }
+    if (tid == 255) s_prefix[n_rows] = off + incl;
+    __syncthreads();
   }
-  sum = wave_sum_i(sum);
-  mx = wave_max_i(mx);
-  if (l == 0) { s_red[w] = sum; s_red[4 + w] = mx; }
-  __syncthreads();
-  sum = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-  mx = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
-  const long long chunks = (long long)sum * n_kv;
-  int split = (int)((chunks + kTargetItems - 1) / kTargetItems);
-  split = max(split, kMinSplitPages);
-  split = max(split, (mx + kMaxSplits - 1) / kMaxSplits);
-  const int s_max = (mx + split - 1) / split;
-  const long long n_items = (long long)n_rows * s_max * n_kv;
+  const long long U = s_prefix[n_rows];
+  const int Gd = gridDim.x;
+  const int gi = blockIdx.x;
+  const long long u0 = range_begin(gi, U, Gd);
+  const long long u1 = range_begin(gi + 1, U, Gd);
+  if (u0 >= u1) return;
 
-  const int64_t pool_slots = num_pages * kPageSize;
+  const int64_t pool_slots = P.num_pages * kPageSize;
 
-  for (long long it = blockIdx.x; it < n_items; it += gridDim.x) {
-    const int g = (int)(it % n_kv);
-    const long long r2 = it / n_kv;
-    const int s = (int)(r2 % s_max);
-    const int b = (int)(r2 / s_max);
-    const int pos = positions[b];
-    if (pos < 0 || pos >= max_pos) continue;
+  // row holding u0: last b with prefix[b] <= u0
+  int b = 0;
+  {
+    int lo = 0, hi = n_rows - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_prefix[mid] <= u0) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  }
+
+  long long u = u0;
+  bool first_segment = true;
+  while (u < u1) {
+    while (s_prefix[b + 1] <= u) ++b;   // skip rows without units
+    const int pos = P.positions[b];
     const int np = pos / kPageSize + 1;
-    const int pb = s * split;
-    if (pb >= np) continue;
-    const int pe = min(pb + split, np);
-    const int nsplit = (np + split - 1) / split;
+    const long long base = s_prefix[b];
+    const int g = (int)((u - base) / np);
+    const int p0 = (int)((u - base) % np);
+    const long long seg_begin = base + (long long)g * np;
+    const long long seg_end = seg_begin + np;
+    const long long stop = min(u1, seg_end);
+    const int pe = p0 + (int)(stop - u);
+    const bool whole = (p0 == 0) && (pe == np);
 
-    // query operand: rows 0..3 = heads 4g..4g+3, 8 dims per MFMA step
+    // query operand: rows 0..3 = heads 4g..4g+3; k-slot 8*G4+i of step st = dim 32*G4+8*st+i
     bf16x8 qa[4];
     if (hr < kGroup) {
-      const uint16_t* qp = q + ((int64_t)b * n_q + g * kGroup + hr) * kHeadDim + 32 * G;
+      const uint16_t* qp = P.q + ((int64_t)b * n_q + g * kGroup + hr) * kHeadDim + 32 * G4;
 #pragma unroll
       for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const bf16x8*>(qp + 8 * st);
     } else {
@@ -126,6 +182,9 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) qa[st][i] = (__bf16)0.0f;
     }
+    const uint16_t* kbase = P.k_pool + (int64_t)g * pool_slots * kHeadDim;
+    const uint16_t* vbase = P.v_pool + (int64_t)g * pool_slots * kHeadDim;
+    const int* trow = P.table + (int64_t)b * P.pages_per_row;
 
     float m[kGroup], lsum[kGroup], acc[kGroup][8];
 #pragma unroll
@@ -135,43 +194,43 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
 #pragma unroll
       for (int d = 0; d < 8; ++d) acc[i][d] = 0.f;
     }
-    const uint16_t* kbase = k_pool + (int64_t)g * pool_slots * kHeadDim;
-    const uint16_t* vbase = v_pool + (int64_t)g * pool_slots * kHeadDim;
-    const int* trow = table + (int64_t)b * pages_per_row;
 
-    for (int p = pb; p < pe; ++p) {
+    auto fetch = [&](int p, PageRegs& r) {
       const int64_t page = trow[p];
-      if (page < 0 || page >= num_pages) continue;
-      const int key0 = p * kPageSize + 16 * w;  // position of this wave's first key
-      const uint16_t* krow = kbase + (page * kPageSize + 16 * w + hr) * kHeadDim + 32 * G;
-      bf16x8 kb[4];
+      r.ok = page >= 0 && page < P.num_pages;
+      const int64_t pg = r.ok ? page : 0;
+      const uint16_t* krow = kbase + (pg * kPageSize + 16 * w + hr) * kHeadDim + 32 * G4;
+      const uint16_t* vrow = vbase + (pg * kPageSize + 16 * w + 4 * G4) * kHeadDim + 8 * hr;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) kb[st] = *reinterpret_cast<const bf16x8*>(krow + 8 * st);
-      const uint16_t* vrow = vbase + (page * kPageSize + 16 * w + 4 * G) * kHeadDim + 8 * hr;
-      uint4 vv[4];
+      for (int st = 0; st < 4; ++st) r.k[st] = *reinterpret_cast<const bf16x8*>(krow + 8 * st);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) vv[jj] = *reinterpret_cast<const uint4*>(vrow + jj * kHeadDim);
+      for (int jj = 0; jj < 4; ++jj) r.v[jj] = *reinterpret_cast<const uint4*>(vrow + jj * kHeadDim);
+    };
 
+    auto compute = [&](int p, const PageRegs& r) {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < 4; ++st) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], kb[st], sc, 0, 0, 0);
-
-      // lanes 0..15: sc[i] = score of head i with key key0 + l
-      const bool kvalid = key0 + hr <= pos;
-      float x[kGroup], mn[kGroup], corr[kGroup], pr[kGroup];
+      for (int st = 0; st < 4; ++st) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], r.k[st], sc, 0, 0, 0);
+      // lanes 0..15: sc[i] = score of head i with key p*64 + 16w + lane
+      const int key0 = p * kPageSize + 16 * w;
+      const bool kvalid = r.ok && key0 + hr <= pos;
+      float pr[kGroup];
       bool any_change = false;
+      float corr[kGroup];
 #pragma unroll
       for (int i = 0; i < kGroup; ++i) {
-        x[i] = kvalid ? sc[i] * scale_log2 : -INFINITY;
-        const float pm = lane0(max16(x[i]));
-        mn[i] = fmaxf(m[i], pm);
-        corr[i] = (m[i] == mn[i]) ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn[i]);
-        any_change |= (m[i] != mn[i]);
-        const float ms = (mn[i] == -INFINITY) ? 0.f : mn[i];
-        pr[i] = __builtin_amdgcn_exp2f(x[i] - ms);
+        const float x = kvalid ? sc[i] * P.scale_log2 : -INFINITY;
+        const float pm = lane0(row_max16(x));
+        const float mn = fmaxf(m[i], pm);
+        corr[i] = (m[i] == mn) ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);
+        any_change |= (m[i] != mn);
+        const float ms = (mn == -INFINITY) ? 0.f : mn;
+        pr[i] = __builtin_amdgcn_exp2f(x - ms);
         lsum[i] = lsum[i] * corr[i] + pr[i];
-        m[i] = mn[i];
+        m[i] = mn;
       }
+      if (l < 16) *reinterpret_cast<float4*>(&s_p[w][l][0]) = make_float4(pr[0], pr[1], pr[2], pr[3]);
+      __builtin_amdgcn_wave_barrier();
       if (any_change) {
 #pragma unroll
         for (int i = 0; i < kGroup; ++i)
@@ -180,29 +239,44 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
       }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int src = 4 * G + jj;  // lane holding this key's probabilities
-        const bool vok = key0 + src <= pos;
-        float ph[kGroup];
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i) ph[i] = __shfl(pr[i], src);
+        const int kk = 4 * G4 + jj;
+        const bool vok = r.ok && key0 + kk <= pos;
+        const float4 ph = *reinterpret_cast<const float4*>(&s_p[w][kk][0]);
         float vf[8];
-        vf[0] = bf16_lo(vv[jj].x); vf[1] = bf16_hi(vv[jj].x);
-        vf[2] = bf16_lo(vv[jj].y); vf[3] = bf16_hi(vv[jj].y);
-        vf[4] = bf16_lo(vv[jj].z); vf[5] = bf16_hi(vv[jj].z);
-        vf[6] = bf16_lo(vv[jj].w); vf[7] = bf16_hi(vv[jj].w);
+        vf[0] = bf16_lo(r.v[jj].x); vf[1] = bf16_hi(r.v[jj].x);
+        vf[2] = bf16_lo(r.v[jj].y); vf[3] = bf16_hi(r.v[jj].y);
+        vf[4] = bf16_lo(r.v[jj].z); vf[5] = bf16_hi(r.v[jj].z);
+        vf[6] = bf16_lo(r.v[jj].w); vf[7] = bf16_hi(r.v[jj].w);
 #pragma unroll
-        for (int d = 0; d < 8; ++d) vf[d] = vok ? vf[d] : 0.f;
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i)
-#pragma unroll
-          for (int d = 0; d < 8; ++d) acc[i][d] += ph[i] * vf[d];
+        for (int d = 0; d < 8; ++d) {
+          const float x = vok ? vf[d] : 0.f;
+          acc[0][d] += ph.x * x;
+          acc[1][d] += ph.y * x;
+          acc[2][d] += ph.z * x;
+          acc[3][d] += ph.w * x;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    };
+
+    {
+      PageRegs ra, rb;
+      fetch(p0, ra);
+      for (int p = p0; p < pe; p += 2) {
+        if (p + 1 < pe) fetch(p + 1, rb);
+        compute(p, ra);
+        if (p + 2 < pe) fetch(p + 2, ra);
+        if (p + 1 < pe) compute(p + 1, rb);
       }
     }
 
     // ---- merge the wave's lanes, then the 4 waves
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
-      lsum[i] = sum16(lsum[i]);
+      lsum[i] += __shfl_xor(lsum[i], 8, 16);
+      lsum[i] += __shfl_xor(lsum[i], 4, 16);
+      lsum[i] += __shfl_xor(lsum[i], 2, 16);
+      lsum[i] += __shfl_xor(lsum[i], 1, 16);
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         acc[i][d] += __shfl_xor(acc[i][d], 16);
@@ -236,40 +310,75 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
       A0 += f * s_acc[ww][hi][dd];
       A1 += f * s_acc[ww][hi][dd + 1];
     }
-    float* orow = out + ((int64_t)b * n_q + g * kGroup + hi) * kHeadDim + dd;
-    if (nsplit == 1) {
+    float* orow = P.out + ((int64_t)b * n_q + g * kGroup + hi) * kHeadDim + dd;
+    if (whole) {
       orow[0] = A0 / L;
       orow[1] = A1 / L;
     } else {
-      const int64_t rg = (int64_t)b * n_kv + g;
-      float* part = partials + (rg * kMaxSplits + s) * kPartial + hi * (kHeadDim + 2);
-      if ((tid & 63) == 0) { part[0] = M; part[1] = L; }
-      part[2 + dd] = A0;
-      part[3 + dd] = A1;
-      __threadfence();
+      const int slot = first_segment ? 0 : 1;
+      float* part = P.partials + ((int64_t)gi * 2 + slot) * kPartial + hi * (kHeadDim + 2);
+      if ((tid & 63) == 0) { store_sc1(part, M); store_sc1(part + 1, L); }
+      store_sc1(part + 2 + dd, A0);
+      store_sc1(part + 3 + dd, A1);
+      __builtin_amdgcn_s_waitcnt(0);   // the partial is at the coherence point before the ticket
       __syncthreads();
-      if (tid == 0) s_last = (atomicAdd(&counters[rg], 1) == nsplit - 1);
+      const int rg = b * P.n_kv + g;
+      const int i0 = owner(seg_begin, U, Gd);
+      const int i1 = owner(seg_end - 1, U, Gd);
+      // workgroups with an empty range (fewer units than workgroups) add no partial
+      int count = 0;
+      for (int i = i0; i <= i1; ++i) count += range_begin(i, U, Gd) < range_begin(i + 1, U, Gd);
+      if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(&P.counters[rg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old == count - 1);
+      }
       __syncthreads();
       if (s_last) {
-        __threadfence();
-        const float* base = partials + rg * kMaxSplits * kPartial + hi * (kHeadDim + 2);
         float Mx = -INFINITY;
-        for (int sp = 0; sp < nsplit; ++sp) Mx = fmaxf(Mx, base[sp * kPartial]);
+        for (int i = i0; i <= i1; ++i) {
+          if (range_begin(i, U, Gd) == range_begin(i + 1, U, Gd)) continue;
+          const int k = (i == i0 && range_begin(i0, U, Gd) < seg_begin) ? 1 : 0;
+          Mx = fmaxf(Mx, load_sc1(P.partials + ((int64_t)i * 2 + k) * kPartial + hi * (kHeadDim + 2)));
+        }
         float Lt = 0.f, B0 = 0.f, B1 = 0.f;
-        for (int sp = 0; sp < nsplit; ++sp) {
-          const float* ps = base + sp * kPartial;
-          const float f = (ps[0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ps[0] - Mx);
-          Lt += f * ps[1];
-          B0 += f * ps[2 + dd];
-          B1 += f * ps[3 + dd];
+        for (int i = i0; i <= i1; ++i) {
+          if (range_begin(i, U, Gd) == range_begin(i + 1, U, Gd)) continue;
+          const int k = (i == i0 && range_begin(i0, U, Gd) < seg_begin) ? 1 : 0;
+          const float* ps = P.partials + ((int64_t)i * 2 + k) * kPartial + hi * (kHeadDim + 2);
+          const float mi = load_sc1(ps);
+          const float f = (mi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi - Mx);
+          Lt += f * load_sc1(ps + 1);
+          B0 += f * load_sc1(ps + 2 + dd);
+          B1 += f * load_sc1(ps + 3 + dd);
         }
         orow[0] = B0 / Lt;
         orow[1] = B1 / Lt;
-        if (tid == 0) counters[rg] = 0;
+        if (tid == 0) __hip_atomic_store(&P.counters[rg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    __syncthreads();
+    __syncthreads();   // LDS reuse by the next segment
+    first_segment = false;
+    u = stop;
   }
+}
+
+int grid_for_device() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    // occupancy with a 1024-row prefix table (larger tables only lower the
+    // occupancy; the result stays correct when not every workgroup is resident)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, paged_decode_bf16_kernel, 256,
+                                                     4096) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 2;
+    cached[dev] = std::min(kMaxGrid, cus * per_cu);
+  }
+  return cached[dev];
 }
 
 }  // namespace
@@ -277,22 +386,31 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
 size_t decode_workspace_bytes(int n_rows, int n_kv_heads, int /*pages_per_row*/) {
   const size_t pairs = (size_t)n_rows * n_kv_heads;
   const size_t counters = (pairs * sizeof(int) + 255) / 256 * 256;
-  return counters + pairs * kMaxSplits * kPartial * sizeof(float);
+  return counters + (size_t)kMaxGrid * 2 * kPartial * sizeof(float);
 }
+
+int decode_max_rows() { return kMaxRows; }
 
 hipError_t launch_decode_bf16(hipStream_t stream, const AttnArgs& a) {
   const size_t pairs = (size_t)a.n_queries * a.n_kv_heads;
   const size_t counter_bytes = (pairs * sizeof(int) + 255) / 256 * 256;
-  int* counters = static_cast<int*>(a.workspace);
-  float* partials = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + counter_bytes);
-  long long max_splits = (long long)(a.pages_per_row + kMinSplitPages - 1) / kMinSplitPages;
-  if (max_splits > kMaxSplits) max_splits = kMaxSplits;
-  const long long items = (long long)pairs * max_splits;
-  const int grid = (int)(items < kGridCap ? items : kGridCap);
-  hipLaunchKernelGGL(paged_decode_bf16_kernel, dim3(grid), dim3(256), 0, stream, a.n_queries,
-                     a.n_kv_heads, (const uint16_t*)a.q, (const uint16_t*)a.k_pool,
-                     (const uint16_t*)a.v_pool, a.num_pages, a.table, a.pages_per_row,
-                     a.positions, a.scale * kLog2e, a.out, counters, partials);
+  DecodeParams P;
+  P.n_rows = a.n_queries;
+  P.n_kv = a.n_kv_heads;
+  P.q = (const uint16_t*)a.q;
+  P.k_pool = (const uint16_t*)a.k_pool;
+  P.v_pool = (const uint16_t*)a.v_pool;
+  P.num_pages = a.num_pages;
+  P.table = a.table;
+  P.pages_per_row = a.pages_per_row;
+  P.positions = a.positions;
+  P.scale_log2 = a.scale * kLog2e;
+  P.out = a.out;
+  P.counters = static_cast<int*>(a.workspace);
+  P.partials = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + counter_bytes);
+  const int grid = grid_for_device();
+  const size_t lds = (size_t)(a.n_queries + 1) * sizeof(int);
+  hipLaunchKernelGGL(paged_decode_bf16_kernel, dim3(grid), dim3(256), lds, stream, P);
   return hipGetLastError();
 }
 

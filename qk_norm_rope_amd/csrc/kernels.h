@@ -44,6 +44,7 @@ hipError_t launch_append(hipStream_t stream, const AppendArgs& a);
 
 // Decode: split-K over page ranges with a fused last-arriver merge.
 size_t decode_workspace_bytes(int n_rows, int n_kv_heads, int pages_per_row);
+int decode_max_rows();
 hipError_t launch_decode_bf16(hipStream_t stream, const AttnArgs& a);
 
 // Prefill: MFMA flash attention over 64-token tiles of the pack.

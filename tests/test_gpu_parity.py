@@ -255,3 +255,18 @@ def test_decode_workspace_is_reusable():
     # counters are back at zero after every call
     n_pairs = w.n_decode * 8
     assert int(ws[:4 * n_pairs].view(torch.int32).abs().sum().item()) == 0
+
+
+@pytest.mark.parametrize("positions", [[0], [5, 70], [63, 64, 65], [200] * 3])
+def test_decode_with_fewer_pages_than_workgroups(positions):
+    # far fewer (row, KV head, page) units than resident workgroups: segments cut
+    # into single pages, many workgroups with nothing to do
+    dec = [(b, p) for b, p in enumerate(positions)]
+    w = W.build("few_units", 26, "bf16", num_pages=64, pages_per_row=8, n_table_rows=len(dec),
+                decode=dec)
+    run = Run(w, keep_pre=False)
+    run.step()
+    ref_q, k_rows, v_rows, slots = oracle_append(w)
+    kp, vp = oracle_pools(w, k_rows, v_rows, slots)
+    ref = O.decode(ref_q, w.dtype, kp, vp, w.dtype, w.decode_table, w.step_positions, W.SCALE)
+    assert max_abs_err(run.dec_out.cpu().numpy(), ref) <= TOL_BF16
