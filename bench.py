@@ -26,7 +26,26 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0
+COPY_PROBE_BYTES = 1 << 30
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_2x2048_plus_128rows_hbm_traffic.txt")
+
+
+def measured_traffic(kernel: str, source: str):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    try:
+        kv = dict(line.split(": ", 1) for line in open(TRAFFIC_FILE).read().splitlines()
+                  if line and not line.startswith("#"))
+        sha = hashlib.sha256(open(os.path.join(ROOT, "qk_norm_rope_amd", "csrc", source), "rb").read()).hexdigest()
+        if kv.get(f"{kernel}.source_sha256") != sha:
+            return None
+        return int(float(kv[f"{kernel}.traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def algorithmic_work(w):
@@ -45,12 +64,37 @@ def algorithmic_work(w):
             "prefill_pairs": pre_pairs, "append_bytes": app_bytes}
 
 
-def cpu_baseline(w, sample_rows=64, seed=0):
-    """Oracle decode of a bounded sample of the workload's decode rows on the host cores.
+def oracle_snapshot(w, k_pool, v_pool, sample_rows=128, prefill_tokens=256, seed=0):
+    """Host copies of the pool slots the oracle sample reads, taken from the
+    generator's pre-step pools before any library kernel has run."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(seed)
+    rows = sorted(rng.choice(w.n_decode, size=min(sample_rows, w.n_decode), replace=False).tolist()) \
+        if w.n_decode else []
+    toks = sorted(rng.choice(w.n_prefill, size=min(prefill_tokens, w.n_prefill), replace=False).tolist()) \
+        if w.n_prefill else []
 
-    The sampled rows' pool contents are materialised (outside the timed region)
-    in a compact pool with an identity page table; the timed region is the
-    oracle's decode of those rows.
+    def grab(row, n):
+        sl = torch.as_tensor(w.row_slot_list(row, n), device=k_pool.device)
+        k = k_pool[:, sl].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        v = v_pool[:, sl].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return k, v
+
+    dec = {b: grab(w.decode_row0 + b, int(w.step_positions[b])) for b in rows}
+    pre_rows = sorted(set(int(w.rows[t]) for t in toks))
+    hist = dict(w.history)
+    pre = {r: grab(r, hist.get(r, 0)) for r in pre_rows}
+    return {"rows": rows, "toks": toks, "dec": dec, "pre": pre}
+
+
+def cpu_baseline(w, snap, passes=4):
+    """The oracle on a bounded sample of the workload, on the host cores.
+
+    Decode: the sampled decode rows, ``passes`` times. Prefill: the sampled
+    prompt tokens. The oracle computes the step's own q/k/v rows itself; the
+    history comes from the snapshot; the timed regions are the oracle's
+    attention calls only.
     """
     import numpy as np
     import oracle as O
@@ -60,35 +104,64 @@ def cpu_baseline(w, sample_rows=64, seed=0):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    rng = np.random.default_rng(seed)
-    rows = sorted(rng.choice(w.n_decode, size=min(sample_rows, w.n_decode), replace=False).tolist())
+    rows, toks = snap["rows"], snap["toks"]
     P = w.n_prefill
-    every_at = np.concatenate([w.positions, w.step_positions]).astype(np.int64)
-    sel = [P + b for b in rows]
-    q_out, k_rows, v_rows = O.append(w.q[sel], w.k[sel], w.v[sel], w.dtype, w.dtype,
-                                     w.q_gain, w.k_gain, every_at[sel])
-    pos_s = w.step_positions[rows].astype(np.int64)
-    ppr = -(-(int(pos_s.max()) + 1) // 64)
-    table = np.arange(len(rows) * ppr, dtype=np.int32).reshape(len(rows), ppr)
-    kp = np.zeros((8, len(rows) * ppr * 64, 128), np.uint16)
-    vp = np.zeros_like(kp)
-    for i, b in enumerate(rows):
-        n = int(pos_s[i])          # history positions 0..n-1, then the row's new token
-        slots = w.row_slot_list(w.decode_row0 + b, n)
-        base = i * ppr * 64
-        for g in range(8):
-            kp[g, base:base + n] = W.host_history(w, 0, g, slots)
-            vp[g, base:base + n] = W.host_history(w, 1, g, slots)
-        kp[:, base + n] = k_rows[i]
-        vp[:, base + n] = v_rows[i]
-    t0 = time.perf_counter()
-    O.decode(q_out, w.dtype, kp, vp, w.dtype, table, pos_s, W.SCALE)
-    dt = time.perf_counter() - t0
-    nbytes = int((pos_s + 1).sum()) * 8 * 128 * 2 * 2
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"float64 oracle decode of {len(rows)} of the {w.n_decode} decode rows "
-                      f"({int((pos_s + 1).sum())} visible positions, {nbytes / 1e9:.3f} GB of K/V)"}
+    res = {"unit": "GB/s", "cores": int(cores), "kind": "oracle"}
+    if rows:
+        every_at = np.concatenate([w.positions, w.step_positions]).astype(np.int64)
+        sel = [P + b for b in rows]
+        q_out, k_rows, v_rows = O.append(w.q[sel], w.k[sel], w.v[sel], w.dtype, w.dtype,
+                                         w.q_gain, w.k_gain, every_at[sel])
+        pos_s = w.step_positions[rows].astype(np.int64)
+        ppr = -(-(int(pos_s.max()) + 1) // 64)
+        table = np.arange(len(rows) * ppr, dtype=np.int32).reshape(len(rows), ppr)
+        kp = np.zeros((8, len(rows) * ppr * 64, 128), np.uint16)
+        vp = np.zeros_like(kp)
+        for i, b in enumerate(rows):
+            n = int(pos_s[i])      # history positions 0..n-1, then the row's new token
+            base = i * ppr * 64
+            kp[:, base:base + n], vp[:, base:base + n] = snap["dec"][b]
+            kp[:, base + n] = k_rows[i]
+            vp[:, base + n] = v_rows[i]
+        t0 = time.perf_counter()
+        for _ in range(passes):
+            O.decode(q_out, w.dtype, kp, vp, w.dtype, table, pos_s, W.SCALE)
+        dt = (time.perf_counter() - t0) / passes
+        del kp, vp
+        nbytes = int((pos_s + 1).sum()) * 8 * 128 * 2 * 2
+        res.update({"value": round(nbytes / dt / 1e9, 4), "seconds": round(dt * passes, 3),
+                    "sample": f"float64 oracle decode of {len(rows)} of the {w.n_decode} decode rows "
+                              f"({int((pos_s + 1).sum())} visible positions, {nbytes / 1e9:.3f} GB of K/V), "
+                              f"{passes} passes"})
+    if toks:
+        q_pre, k_pre, v_pre = O.append(w.q[:P], w.k[:P], w.v[:P], w.dtype, w.dtype, w.q_gain,
+                                       w.k_gain, w.positions)
+        pre_rows = sorted(snap["pre"])
+        nvis = {r: max(int(w.positions[t]) for t in toks if int(w.rows[t]) == r) + 1 for r in pre_rows}
+        ppr2 = max(-(-n // 64) for n in nvis.values())
+        tab2 = np.zeros((max(pre_rows) + 1, ppr2), np.int32)
+        kp2 = np.zeros((8, len(pre_rows) * ppr2 * 64, 128), np.uint16)
+        vp2 = np.zeros_like(kp2)
+        for i, r in enumerate(pre_rows):
+            base = i * ppr2 * 64
+            kh, vh = snap["pre"][r]
+            kp2[:, base:base + kh.shape[1]] = kh
+            vp2[:, base:base + vh.shape[1]] = vh
+            tab2[r] = np.arange(i * ppr2, (i + 1) * ppr2)
+        # the chunk's own keys/values, as the oracle computed them, at their positions
+        for t in range(P):
+            r = int(w.rows[t])
+            if r in nvis and int(w.positions[t]) < nvis[r]:
+                base = pre_rows.index(r) * ppr2 * 64
+                kp2[:, base + int(w.positions[t])] = k_pre[t]
+                vp2[:, base + int(w.positions[t])] = v_pre[t]
+        t0 = time.perf_counter()
+        O.prefill(q_pre, w.dtype, kp2, vp2, w.dtype, tab2, w.rows, w.positions, W.SCALE, tokens=toks)
+        dtp = time.perf_counter() - t0
+        flops = sum(int(w.positions[t]) + 1 for t in toks) * 4 * 128 * 32
+        res["prefill"] = {"tflops": round(flops / dtp / 1e12, 6), "unit": "TFLOP/s", "seconds": round(dtp, 3),
+                          "sample": f"float64 oracle prefill of {len(toks)} of the {P} prompt tokens"}
+    return res
 
 
 def main():
@@ -98,6 +171,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4, help="standard workload index (default: mixed step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path has no "
@@ -118,6 +193,7 @@ def main():
         sys.exit(2)
     t = W.upload(w, dev)
     k_pool, v_pool = W.make_pools(w, dev)
+    snap = None if args.no_cpu_baseline else oracle_snapshot(w, k_pool, v_pool)
     cos, sin = Q.rope_table(1e6, W.MAX_POSITIONS)
     cos, sin = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
     P, R = w.n_prefill, w.n_decode
@@ -149,6 +225,14 @@ def main():
                                 W.SCALE, dec_out, ws_d)
         if timed:
             ev[3].record(stream)
+
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step(False)
@@ -192,7 +276,8 @@ def main():
                    "pool_pages": w.num_pages, "page_size": 64, "q_heads": 32, "kv_heads": 8,
                    "head_dim": 128},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("paged_decode_bf16_kernel", "decode.hip") if args.workload == 4 else None,
                      "kernel": "paged_decode_bf16_kernel",
                      "bytes_per_launch": work["decode_bytes"], "ms_per_launch": round(times["decode"], 5)},
         "prefill": {"tflops": round(pre_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -203,7 +288,7 @@ def main():
                    "bound": "hbm"},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"] = cpu_baseline(w, snap)
     print(json.dumps(result), flush=True)
 
 

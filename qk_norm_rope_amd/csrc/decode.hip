@@ -334,22 +334,33 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(DecodeParams P) 
       }
       __syncthreads();
       if (s_last) {
-        float Mx = -INFINITY;
-        for (int i = i0; i <= i1; ++i) {
-          if (range_begin(i, U, Gd) == range_begin(i + 1, U, Gd)) continue;
-          const int k = (i == i0 && range_begin(i0, U, Gd) < seg_begin) ? 1 : 0;
-          Mx = fmaxf(Mx, load_sc1(P.partials + ((int64_t)i * 2 + k) * kPartial + hi * (kHeadDim + 2)));
-        }
-        float Lt = 0.f, B0 = 0.f, B1 = 0.f;
-        for (int i = i0; i <= i1; ++i) {
-          if (range_begin(i, U, Gd) == range_begin(i + 1, U, Gd)) continue;
-          const int k = (i == i0 && range_begin(i0, U, Gd) < seg_begin) ? 1 : 0;
-          const float* ps = P.partials + ((int64_t)i * 2 + k) * kPartial + hi * (kHeadDim + 2);
-          const float mi = load_sc1(ps);
-          const float f = (mi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi - Mx);
-          Lt += f * load_sc1(ps + 1);
-          B0 += f * load_sc1(ps + 2 + dd);
-          B1 += f * load_sc1(ps + 3 + dd);
+        // one pass over the partials in workgroup order, 8 partials' loads in flight at a time
+        const bool i0_first = range_begin(i0, U, Gd) >= seg_begin;
+        float Mx = -INFINITY, Lt = 0.f, B0 = 0.f, B1 = 0.f;
+        for (int ib = i0; ib <= i1; ib += 8) {
+          float mv[8], lv[8], x0[8], x1[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int i = ib + k;
+            const bool ok = i <= i1 && range_begin(i, U, Gd) < range_begin(i + 1, U, Gd);
+            const int slot = (i == i0 && !i0_first) ? 1 : 0;
+            const float* ps = P.partials + ((int64_t)(ok ? i : i0) * 2 + slot) * kPartial + hi * (kHeadDim + 2);
+            mv[k] = ok ? load_sc1(ps) : -INFINITY;
+            lv[k] = ok ? load_sc1(ps + 1) : 0.f;
+            x0[k] = ok ? load_sc1(ps + 2 + dd) : 0.f;
+            x1[k] = ok ? load_sc1(ps + 3 + dd) : 0.f;
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            if (mv[k] == -INFINITY) continue;
+            const float mn = fmaxf(Mx, mv[k]);
+            const float fo = (Mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mx - mn);
+            const float fi = __builtin_amdgcn_exp2f(mv[k] - mn);
+            Lt = Lt * fo + lv[k] * fi;
+            B0 = B0 * fo + x0[k] * fi;
+            B1 = B1 * fo + x1[k] * fi;
+            Mx = mn;
+          }
         }
         orow[0] = B0 / Lt;
         orow[1] = B1 / Lt;
