@@ -159,6 +159,8 @@ size_t paged_decode_attn_workspace(const qkr_pool* pool, int32_t n_rows, int32_t
  * tokens and handles blocks that span several rows.
  *
  * rows, positions: device int32 [n_tokens]; rows[p] in [0, n_table_rows).
+ * A bfloat16 pool takes tables of at most 2048 pages per row (131072 positions;
+ * QKR_EUNSUPPORTED above).
  * out: float32 [n_tokens][num_q_heads*head_dim].
  * workspace: at least paged_prefill_attn_workspace() bytes (holds the tile
  * schedule); contents need no initialisation.

@@ -11,7 +11,7 @@
 #include <cstdio>
 #include <cstdint>
 
-#include "../../include/qknr.h"
+#include "qknr.h"
 #include "kernels.h"
 
 namespace {
@@ -178,6 +178,7 @@ int paged_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!a.bf16) return launch_status(qknr::launch_attention_generic(s, a));
+  if (pages_per_row > qknr::prefill_max_pages_per_row()) return QKR_EUNSUPPORTED;
   const size_t need = qknr::prefill_workspace_bytes(n_tokens, pool->num_kv_heads);
   if (!workspace || workspace_bytes < need) return QKR_EWORKSPACE;
   return launch_status(qknr::launch_prefill_bf16(s, a));

@@ -49,6 +49,7 @@ hipError_t launch_decode_bf16(hipStream_t stream, const AttnArgs& a);
 
 // Prefill: MFMA flash attention over 64-token tiles of the pack.
 size_t prefill_workspace_bytes(int n_tokens, int n_kv_heads);
+int prefill_max_pages_per_row();
 hipError_t launch_prefill_bf16(hipStream_t stream, const AttnArgs& a);
 
 // One workgroup per (query, KV head); any pool dtype. Used for float32 pools.

@@ -97,20 +97,60 @@ __device__ __forceinline__ bf16x8 join(i16x4 a, i16x4 b) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Waves w and w+4 share a SIMD: w < 4 is group A (queries 0..31 of the tile),
-// w >= 4 group B (queries 32..63), both for query head 4g + (w & 3). Between two
-// workgroup barriers ("phases") one group issues MFMAs while the other runs the
-// softmax, so each SIMD's matrix core and vector ALU work at the same time:
-//   group A, phase 2j  : O += V(j-1).P(j-1);  S(j) = K(j).Q   (MFMA)
-//   group A, phase 2j+1: mask + softmax of S(j) -> P(j)      (VALU)
-//   group B runs the same sequence one phase later.
-// Page j's K is read in phases 2j..2j+1 and its V in 2j+2..2j+3, so three LDS
-// page buffers suffice; page j+1 is fetched in phase 2j and stored in 2j+1.
+// s_waitcnt vmcnt(n) (gfx9 encoding), leaving the other counters alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS page layout: row r of a K page starts at r * kKRow bytes, row r of a V
+// page at r * kVRow bytes (256 bytes of data, the rest padding). The 16-byte K
+// reads of 16 consecutive rows then land on 16 distinct 4-bank groups, and the
+// 8-byte transposed V reads of 4 consecutive rows by 32 lanes cover all 64 banks
+// once. Rows are copied with 4-byte LDS-direct loads (one 256-byte row per wave
+// instruction), so every row can start at its padded offset.
+constexpr int kKRow = 256 + 16;
+constexpr int kVRow = 256 + 64;
+constexpr int kKPageBytes = kTile * kKRow;
+constexpr int kVPageBytes = kTile * kVRow;
+constexpr int kBuffers = 3;
+
+constexpr int kTabCache = 2048;   // page ids of a run kept in LDS (pages_per_row at most)
+
+// Three K/V page buffers as separate LDS objects: every buffer index below is a
+// compile-time constant, so the compiler can tell a page being copied in from the
+// page being read and does not wait for the copy before the reads.
+__shared__ __attribute__((aligned(1024))) uint8_t sK0[kKPageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t sK1[kKPageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t sK2[kKPageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t sV0[kVPageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t sV1[kVPageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t sV2[kVPageBytes];
+
+template <int B> __device__ __forceinline__ uint8_t* kbuf() { return B == 0 ? sK0 : (B == 1 ? sK1 : sK2); }
+template <int B> __device__ __forceinline__ uint8_t* vbuf() { return B == 0 ? sV0 : (B == 1 ? sV1 : sV2); }
+template <int B> struct Buf { static constexpr int value = B; };
+
+// Workgroup barrier for the page loop. The only LDS writes in flight are the
+// page copies, which the caller has already waited for (vmcnt), so no fence on
+// global memory is needed; the signal fences keep the compiler from moving LDS
+// reads across the barrier.
+__device__ __forceinline__ void page_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Eight waves: wave w is query head 4g + (w & 3) for the 32 queries
+// 32*(w >> 2) .. +31 of the tile, two waves per SIMD. Pages are copied straight
+// from HBM into LDS (global_load_lds) one page ahead of the computation.
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void paged_prefill_bf16_kernel(PrefillParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[3][kTile * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[3][kTile * kVStride];
   __shared__ int sRow[kTile], sPos[kTile];
+  __shared__ int sTab[kTabCache];
 
   const int n_q = P.n_kv * kGroup;
   const int item = blockIdx.x;
@@ -121,9 +161,8 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
   const int l = tid & 63;
   const int lq = l & 31;        // query index within the wave's 32 queries
   const int lh = l >> 5;        // half of the wave
-  const int grp = w >> 2;       // 0: group A, 1: group B (one phase later)
   const int head = g * kGroup + (w & 3);
-  const int qn = 32 * grp + lq; // the lane's query within the tile
+  const int qn = 32 * (w >> 2) + lq;   // the lane's query within the tile
   const int t0 = tile * kTile;
   const int max_pos = P.pages_per_row * kPageSize;
 
@@ -163,6 +202,7 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
   const float sc = P.scale_log2;
   const int G4 = l >> 4;
   const int jj = l & 15;
+  const int vlane = (4 * lh + (jj >> 2)) * kVRow + 8 * (4 * (G4 & 1) + (jj & 3));
 
   int a = 0;
   while (a < kTile) {
@@ -176,6 +216,14 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
     maxp = uniform(maxp);
     const int npages = maxp / kPageSize + 1;
     const int* trow = P.table + (int64_t)r * P.pages_per_row;
+    for (int i = tid; i < npages; i += 512) sTab[i] = trow[i];
+    // every position <= maxp of the row holds finite data; masked keys past maxp
+    // are fetched from this slot instead (their probability is exactly 0)
+    const int64_t last_page = trow[maxp / kPageSize];
+    const int64_t fill_slot = (last_page >= 0 && last_page < P.num_pages)
+                                  ? last_page * kPageSize + maxp % kPageSize : 0;
+    __syncthreads();
+    auto page_of = [&](int p) -> int64_t { return p < npages ? sTab[p] : -1; };
 
     const bool active = qn >= a && qn < e;
     // smallest position among the wave's queries; -1 when some query is not in this run
@@ -184,143 +232,149 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
     for (int mm = 32; mm >= 1; mm >>= 1) wmin = min(wmin, __shfl_xor(wmin, mm));
     wmin = uniform(wmin);
 
-    float m = -INFINITY;     // running max of scale*log2(e)*score, per query
-    float lsum = 0.f;        // this lane's share of the softmax denominator
+    float m = -INFINITY;
+    float lsum = 0.f;
     f32x16 o[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-    f32x16 st[2];
-    bf16x8 pb[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[c][i] = (__bf16)0.0f;
 
-    // staging: 1024 chunks of 16 bytes for K and for V, 2 per thread
-    uint4 kr[2], vr[2];
-    auto fetch = [&](int p) {
-      const int64_t page = trow[p];
+    // copy page p into buffer B: wave w moves rows 8w..8w+7 of K and of V, one
+    // 256-byte row per instruction (16 copies). Pages past the run copy its last
+    // valid row instead, so every step issues the same copies (the compiler then
+    // tracks which buffer each copy targets).
+    auto fetch = [&](auto Bc, int p) {
+      constexpr int B = decltype(Bc)::value;
+      const int64_t page = page_of(p);
       const bool ok = page >= 0 && page < P.num_pages;
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int c = tid + 512 * rr;
-        const int key = c >> 4;
-        const int c16 = c & 15;
-        if (ok && p * kPageSize + key <= maxp) {
-          const int64_t off = (page * kPageSize + key) * kHeadDim + c16 * 8;
-          kr[rr] = *reinterpret_cast<const uint4*>(kbase + off);
-          vr[rr] = *reinterpret_cast<const uint4*>(vbase + off);
-        } else {
-          kr[rr] = make_uint4(0, 0, 0, 0);
-          vr[rr] = make_uint4(0, 0, 0, 0);
-        }
-      }
-    };
-    auto stage = [&](int buf) {
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int c = tid + 512 * rr;
-        const int key = c >> 4;
-        const int c16 = c & 15;
-        *reinterpret_cast<uint4*>(&sK[buf][key * kKStride + c16 * 8]) = kr[rr];
-        *reinterpret_cast<uint4*>(&sV[buf][key * kVStride + c16 * 8]) = vr[rr];
+      for (int i = 0; i < 8; ++i) {
+        const int row = 8 * w + i;
+        const bool rok = ok && p * kPageSize + row <= maxp;
+        const int64_t slot = rok ? page * kPageSize + row : fill_slot;
+        const uint16_t* kg = kbase + slot * kHeadDim + 2 * l;
+        const uint16_t* vg = vbase + slot * kHeadDim + 2 * l;
+        __builtin_amdgcn_global_load_lds(kg, (lds_void*)(kbuf<B>() + row * kKRow), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(vg, (lds_void*)(vbuf<B>() + row * kVRow), 4, 0, 0);
       }
     };
 
-    fetch(0);
-    stage(0);
-    __syncthreads();
-
-    const int n_phases = 2 * npages + 2;
-    for (int ph = 0; ph < n_phases; ++ph) {
-      const int jn = ph >> 1;                  // page staged during this phase pair: jn + 1
-      if (!(ph & 1) && jn + 1 < npages) fetch(jn + 1);
-      const int my = ph - grp;                 // this group's own phase
-      if (my >= 0) {
-        const int j = my >> 1;
-        if (!(my & 1)) {
-          // ---- MFMA phase: O += V(j-1) . P(j-1), then S(j) = K(j) . Q
-          if (j >= 1) {
-            const uint16_t* vl = &sV[(j - 1) % 3][0];
+    // ---- S(j) = K(j) . Q^T into st
+    f32x16 st[2];
+    auto qk = [&](auto KBc, int j) {
+      constexpr int KB = decltype(KBc)::value;
+      const uint8_t* kl = kbuf<KB>();
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const int keyA = 16 * c + 4 * lh;
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-              for (int dt = 0; dt < 4; ++dt) {
-                const int dim0 = 32 * dt + 16 * (G4 & 1);
-                const uint16_t* pa = vl + (keyA + (jj >> 2)) * kVStride + dim0 + 4 * (jj & 3);
-                const i16x4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pa);
-                const i16x4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa + 8 * kVStride));
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(ra, rb), pb[c], o[dt], 0, 0, 0);
-              }
-            }
-          }
-          if (j < npages) {
-            const uint16_t* kl = &sK[j % 3][0];
+        for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+      for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
-              for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-              for (int kt = 0; kt < 2; ++kt) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + (kt * 32 + lq) * kKStride + 16 * ks + 8 * lh);
-                st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], st[kt], 0, 0, 0);
-              }
-            }
-          }
-        } else if (j < npages) {
-          // ---- VALU phase: mask, online softmax of S(j) -> P(j)
-          const int kpos0 = j * kPageSize;
-          const int64_t page = trow[j];
-          const bool pok = page >= 0 && page < P.num_pages;
-          if (!pok || wmin < kpos0 + kPageSize - 1) {
-            const int lim = (active && pok) ? qpos - kpos0 : -1;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-              for (int rg = 0; rg < 16; ++rg) {
-                const int key = kt * 32 + 8 * (rg >> 2) + 4 * lh + (rg & 3);
-                st[kt][rg] = (key <= lim) ? st[kt][rg] : -INFINITY;
-              }
-          }
-          float mx = -INFINITY;
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int rg = 0; rg < 16; ++rg) mx = fmaxf(mx, st[kt][rg]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
-          const bool need = mx > m + kRescaleThreshold;
-          const float mn = need ? mx : m;
-          const float corr = need ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
-          const float ms = (mn == -INFINITY) ? 0.f : mn;
-          float ps = 0.f;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-#pragma unroll
-            for (int ii = 0; ii < 8; ++ii) {
-              const int rg = 4 * (2 * (c & 1) + (ii >> 2)) + (ii & 3);
-              const float ev = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][rg], sc, -ms));
-              ps += ev;
-              pb[c][ii] = (__bf16)ev;
-            }
-          }
-          lsum = lsum * corr + ps;
-          m = mn;
-          if (__any(need)) {
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
-          }
+        for (int kt = 0; kt < 2; ++kt) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + (kt * 32 + lq) * kKRow + 32 * ks + 16 * lh);
+          st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], st[kt], 0, 0, 0);
         }
       }
-      if ((ph & 1) && jn + 1 < npages) stage((jn + 1) % 3);
-      __syncthreads();
+    };
+    // ---- mask + online softmax of st (page j) into pb
+    bf16x8 pb[4];
+    auto softmax = [&](int j) {
+      const int64_t page = page_of(j);
+      const bool pok = page >= 0 && page < P.num_pages;
+      const int kpos0 = j * kPageSize;
+      if (!pok || wmin < kpos0 + kPageSize - 1) {
+        // key index = kt*32 + 8*(rg>>2) + 4*lh + (rg&3); compare the constant part
+        const int lim = ((active && pok) ? qpos - kpos0 : -1) - 4 * lh;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int rg = 0; rg < 16; ++rg)
+            st[kt][rg] = (kt * 32 + 8 * (rg >> 2) + (rg & 3) <= lim) ? st[kt][rg] : -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) mx = fmaxf(mx, st[kt][rg]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+      const bool need = mx > m + kRescaleThreshold;
+      const float mn = need ? mx : m;
+      const float corr = need ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
+      const float ms = (mn == -INFINITY) ? 0.f : mn;
+      float ps = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const int rg = 4 * (2 * (c & 1) + (ii >> 2)) + (ii & 3);
+          const float ev = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][rg], sc, -ms));
+          ps += ev;
+          pb[c][ii] = (__bf16)ev;
+        }
+      }
+      lsum = lsum * corr + ps;
+      m = mn;
+      if (__any(need)) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
+      }
+    };
+    // ---- O += V(j-1) . P(j-1), V^T via transposed LDS reads
+    auto pv = [&](auto VBc) {
+      constexpr int VB = decltype(VBc)::value;
+      const uint8_t* vl = vbuf<VB>();
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          // rows 16c + 4lh + jj/4 (+8), 8-byte granule 8dt + 4(G4&1) + (jj&3) of the row
+          const uint8_t* pa = vl + vlane + (16 * c) * kVRow + 64 * dt;
+          const i16x4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pa);
+          const i16x4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa + 8 * kVRow));
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(ra, rb), pb[c], o[dt], 0, 0, 0);
+        }
+      }
+    };
+
+    // Ping-pong: waves w and w+4 share a SIMD; group 0 (w < 4) and group 1 run
+    // one phase apart, so in every phase one of them issues MFMAs while the
+    // other runs the softmax. For page j (LDS buffer j % 3):
+    //   phase 2j  : group 0 PV(j-1) + S(j)   | group 1 softmax(j-1)
+    //   phase 2j+1: group 0 softmax(j)       | group 1 PV(j-1) + S(j)
+    // Page j+1 is copied in during phases 2j..2j+1 into the buffer page j-2 used.
+    const int grp = w >> 2;
+    auto mfma_phase = [&](auto KBc, auto VBc, int j) {
+      if (j >= 1 && j - 1 < npages) pv(VBc);
+      if (j < npages) qk(KBc, j);
+    };
+    auto phase_even = [&](auto KBc, auto VBc, auto NBc, int j) {
+      wait_vmcnt<0>();        // page j's copies (issued two phases ago) are in LDS
+      page_barrier();
+      fetch(NBc, j + 1);
+      if (grp == 0) mfma_phase(KBc, VBc, j);
+      else if (j >= 1 && j - 1 < npages) softmax(j - 1);
+    };
+    auto phase_odd = [&](auto KBc, auto VBc, int j) {
+      page_barrier();
+      if (grp == 0) { if (j < npages) softmax(j); }
+      else mfma_phase(KBc, VBc, j);
+    };
+
+    fetch(Buf<0>{}, 0);
+    for (int j = 0; j <= npages; j += 3) {
+      phase_even(Buf<0>{}, Buf<2>{}, Buf<1>{}, j);
+      phase_odd(Buf<0>{}, Buf<2>{}, j);
+      phase_even(Buf<1>{}, Buf<0>{}, Buf<2>{}, j + 1);
+      phase_odd(Buf<1>{}, Buf<0>{}, j + 1);
+      phase_even(Buf<2>{}, Buf<1>{}, Buf<0>{}, j + 2);
+      phase_odd(Buf<2>{}, Buf<1>{}, j + 2);
     }
+    wait_vmcnt<0>();
+    __syncthreads();   // all reads of the page buffers and sTab are done before the next run
 
     // ---- normalise and store: lane holds dims 32dt + 8j + 4lh + i of its query
     const float lt = lsum + __shfl_xor(lsum, 32);
@@ -342,6 +396,8 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
 }
 
 }  // namespace
+
+int prefill_max_pages_per_row() { return kTabCache; }
 
 size_t prefill_workspace_bytes(int n_tokens, int /*n_kv_heads*/) {
   const size_t tiles = (size_t)(n_tokens + kTile - 1) / kTile;
