@@ -96,6 +96,26 @@ __device__ __forceinline__ bf16x8 join(i16x4 a, i16x4 b) {
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Marks x as produced at this point. The page loop's barriers order memory only,
+// so without this the compiler may sink a phase's register-only work (softmax,
+// MFMAs) past the barrier to its consumer and undo the two-group interleave.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
+
+// Raw buffer descriptor over one K or V page of one KV head (64 rows x 256 bytes).
+// Word 3 selects 32-bit data format, as the LDS-direct dword loads need; reads past
+// the page return zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* page_base) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)page_base, 0, kPageSize * kHeadDim * 2, 0x00020000);
+}
 
 // s_waitcnt vmcnt(n) (gfx9 encoding), leaving the other counters alone
 template <int N>
@@ -106,17 +126,37 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS page layout: row r of a K page starts at r * kKRow bytes, row r of a V
-// page at r * kVRow bytes (256 bytes of data, the rest padding). The 16-byte K
-// reads of 16 consecutive rows then land on 16 distinct 4-bank groups, and the
-// 8-byte transposed V reads of 4 consecutive rows by 32 lanes cover all 64 banks
-// once. Rows are copied with 4-byte LDS-direct loads (one 256-byte row per wave
-// instruction), so every row can start at its padded offset.
-constexpr int kKRow = 256 + 16;
-constexpr int kVRow = 256 + 64;
-constexpr int kKPageBytes = kTile * kKRow;
-constexpr int kVPageBytes = kTile * kVRow;
-constexpr int kBuffers = 3;
+// Instruction order for the fused MFMA stream (scheduler groups): the LDS reads of
+// the first A operands, then every MFMA followed by the reads of the operand A
+// places later. Operands 0..15 take two transposed reads, 16..31 one 16-byte read.
+template <int A, int I = 0>
+__device__ __forceinline__ void fused_order() {
+  if constexpr (I < A) {
+    __builtin_amdgcn_sched_group_barrier(0x100, I < 16 ? 2 : 1, 0);
+    fused_order<A, I + 1>();
+  } else if constexpr (I < A + 32) {
+    constexpr int m = I - A;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (m + A < 32) __builtin_amdgcn_sched_group_barrier(0x100, m + A < 16 ? 2 : 1, 0);
+    fused_order<A, I + 1>();
+  }
+}
+
+// LDS page layout: 64 rows of 256 bytes (16 chunks of 16 bytes) with the chunks
+// of each row permuted by an XOR swizzle, so that the MFMA operand reads hit
+// every bank once per cycle:
+//   K: chunk c of row r sits at chunk c ^ (r & 15). A 16-byte read of one chunk
+//      by 16 consecutive rows touches 16 distinct chunk positions.
+//   V: chunk c of row r sits at chunk c ^ 4(r & 3). The transposed 8-byte reads
+//      take 64 bytes (4 chunks) from each of 4 consecutive rows; the swizzle puts
+//      the 4 rows in the 4 different 64-byte quarters of the bank space.
+// A page is copied with 16-byte LDS-direct loads: one wave instruction fills 1 KB
+// (4 rows) linearly, each lane fetching the global chunk that belongs at its slot.
+constexpr int kRowBytes = kHeadDim * 2;
+constexpr int kKPageBytes = kTile * kRowBytes;
+constexpr int kVPageBytes = kTile * kRowBytes;
+__device__ __forceinline__ int k_swz(int r) { return r & 15; }
+__device__ __forceinline__ int v_swz(int r) { return 4 * (r & 3); }
 
 constexpr int kTabCache = 2048;   // page ids of a run kept in LDS (pages_per_row at most)
 
@@ -200,9 +240,23 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
   const uint16_t* kbase = P.k_pool + (int64_t)g * pool_slots * kHeadDim;
   const uint16_t* vbase = P.v_pool + (int64_t)g * pool_slots * kHeadDim;
   const float sc = P.scale_log2;
-  const int G4 = l >> 4;
+  // K operand (S^T = K . Q^T): lane reads row kt*32 + lq, chunk 2*ks + lh;
+  // byte offset of ks's chunk in rows kt*32 + lq (kt adds 32 rows)
+  int kofs[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) kofs[ks] = lq * kRowBytes + (((2 * ks + lh) ^ k_swz(lq)) << 4);
+  // V^T operand (transposed reads): lane reads 8 bytes of row 16c + 8h + 4lh + jj/4,
+  // dims 32dt + 16(G4 & 1) + 4(jj & 3) .. +3, i.e. chunk 4dt + 2(G4 & 1) + (jj & 3)/2
   const int jj = l & 15;
-  const int vlane = (4 * lh + (jj >> 2)) * kVRow + 8 * (4 * (G4 & 1) + (jj & 3));
+  const int vrow = 4 * lh + (jj >> 2);
+  int vofs[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    vofs[dt] = vrow * kRowBytes + (((4 * dt + 2 * ((l >> 4) & 1) + ((jj & 3) >> 1)) ^ v_swz(vrow)) << 4) + 8 * (jj & 1);
+  // page copy: instruction q of the wave fills rows 4(2w + q) .. +3; lane i takes
+  // row 4(2w + q) + i/16 and the global chunk that belongs at slot i % 16
+  const int crow0 = 8 * w + (l >> 4);
+  const int cslot = l & 15;
 
   int a = 0;
   while (a < kTile) {
@@ -216,14 +270,22 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
     maxp = uniform(maxp);
     const int npages = maxp / kPageSize + 1;
     const int* trow = P.table + (int64_t)r * P.pages_per_row;
-    for (int i = tid; i < npages; i += 512) sTab[i] = trow[i];
+    bool bad = false;
+    for (int i = tid; i < npages; i += 512) {
+      const int id = trow[i];
+      sTab[i] = id;
+      bad |= id < 0 || id >= P.num_pages;
+    }
     // every position <= maxp of the row holds finite data; masked keys past maxp
     // are fetched from this slot instead (their probability is exactly 0)
     const int64_t last_page = trow[maxp / kPageSize];
-    const int64_t fill_slot = (last_page >= 0 && last_page < P.num_pages)
-                                  ? last_page * kPageSize + maxp % kPageSize : 0;
-    __syncthreads();
+    const bool last_ok = last_page >= 0 && last_page < P.num_pages;
+    const int64_t fill_page = uniform64(last_ok ? last_page : 0);
+    const int fill_row = uniform(last_ok ? maxp % kPageSize : 0);
+    // some page of the run is outside the pool: only then does the softmax look pages up
+    const bool any_bad = __syncthreads_or(bad);
     auto page_of = [&](int p) -> int64_t { return p < npages ? sTab[p] : -1; };
+    auto page_ok = [&](int64_t page) { return page >= 0 && page < P.num_pages; };
 
     const bool active = qn >= a && qn < e;
     // smallest position among the wave's queries; -1 when some query is not in this run
@@ -240,49 +302,37 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
-    // copy page p into buffer B: wave w moves rows 8w..8w+7 of K and of V, one
-    // 256-byte row per instruction (16 copies). Pages past the run copy its last
-    // valid row instead, so every step issues the same copies (the compiler then
-    // tracks which buffer each copy targets).
-    auto fetch = [&](auto Bc, int p) {
+    // copy page p into buffer B: wave w moves rows 8w..8w+7 of K and of V with two
+    // 1 KB instructions each. Rows past the run's last position, and pages past
+    // the run or outside the pool, copy the run's last valid row instead (finite
+    // data; those keys are masked), so every step issues the same copies and the
+    // compiler tracks which buffer each copy targets. The page is addressed
+    // through a buffer descriptor (reads past the page return zero).
+    auto fetch = [&](auto Bc, int p, int64_t page) {
       constexpr int B = decltype(Bc)::value;
-      const int64_t page = page_of(p);
-      const bool ok = page >= 0 && page < P.num_pages;
+      page = uniform64(page);
+      const bool ok = page_ok(page);
+      const int64_t src = ok ? page : fill_page;
+      const int lim = ok ? maxp - p * kPageSize : -1;   // rows <= lim hold real keys
+      const __amdgpu_buffer_rsrc_t rk = page_rsrc(kbase + src * kPageSize * kHeadDim);
+      const __amdgpu_buffer_rsrc_t rv = page_rsrc(vbase + src * kPageSize * kHeadDim);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = 8 * w + i;
-        const bool rok = ok && p * kPageSize + row <= maxp;
-        const int64_t slot = rok ? page * kPageSize + row : fill_slot;
-        const uint16_t* kg = kbase + slot * kHeadDim + 2 * l;
-        const uint16_t* vg = vbase + slot * kHeadDim + 2 * l;
-        __builtin_amdgcn_global_load_lds(kg, (lds_void*)(kbuf<B>() + row * kKRow), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(vg, (lds_void*)(vbuf<B>() + row * kVRow), 4, 0, 0);
+      for (int q = 0; q < 2; ++q) {
+        const int row = crow0 + 4 * q;
+        const int srow = row <= lim ? row : fill_row;
+        const int ko = srow * kRowBytes + ((cslot ^ k_swz(row)) << 4);
+        const int vo = srow * kRowBytes + ((cslot ^ v_swz(row)) << 4);
+        const int dst = (8 * uniform(w) + 4 * q) * kRowBytes;   // scalar LDS offset
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kbuf<B>() + dst), 16, ko, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vbuf<B>() + dst), 16, vo, 0, 0, 0);
       }
     };
 
-    // ---- S(j) = K(j) . Q^T into st
-    f32x16 st[2];
-    auto qk = [&](auto KBc, int j) {
-      constexpr int KB = decltype(KBc)::value;
-      const uint8_t* kl = kbuf<KB>();
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + (kt * 32 + lq) * kKRow + 32 * ks + 16 * lh);
-          st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], st[kt], 0, 0, 0);
-        }
-      }
-    };
+    f32x16 st[2];   // S^T of the page: keys x queries
     // ---- mask + online softmax of st (page j) into pb
     bf16x8 pb[4];
     auto softmax = [&](int j) {
-      const int64_t page = page_of(j);
-      const bool pok = page >= 0 && page < P.num_pages;
+      const bool pok = !any_bad || page_ok(uniform64(page_of(j)));
       const int kpos0 = j * kPageSize;
       if (!pok || wmin < kpos0 + kPageSize - 1) {
         // key index = kt*32 + 8*(rg>>2) + 4*lh + (rg&3); compare the constant part
@@ -298,48 +348,49 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int rg = 0; rg < 16; ++rg) mx = fmaxf(mx, st[kt][rg]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+      {
+        // the other half of the query's keys sits in lane l ^ 32
+        const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
+                                                         __builtin_bit_cast(unsigned, mx), false, false);
+        mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * sc;
+      }
       const bool need = mx > m + kRescaleThreshold;
       const float mn = need ? mx : m;
       const float corr = need ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
       const float ms = (mn == -INFINITY) ? 0.f : mn;
-      float ps = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
 #pragma unroll
         for (int ii = 0; ii < 8; ++ii) {
           const int rg = 4 * (2 * (c & 1) + (ii >> 2)) + (ii & 3);
-          const float ev = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][rg], sc, -ms));
-          ps += ev;
-          pb[c][ii] = (__bf16)ev;
+          pb[c][ii] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][rg], sc, -ms));
         }
       }
+      // the normaliser sums the bfloat16 weights that enter P.V (two per dot2)
+      float ps = 0.f;
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int ii = 0; ii < 8; ii += 2) {
+          const bf16x2 pr = {pb[c][ii], pb[c][ii + 1]};
+          ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
+        }
       lsum = lsum * corr + ps;
       m = mn;
       if (__any(need)) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
-      }
-    };
-    // ---- O += V(j-1) . P(j-1), V^T via transposed LDS reads
-    auto pv = [&](auto VBc) {
-      constexpr int VB = decltype(VBc)::value;
-      const uint8_t* vl = vbuf<VB>();
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          // rows 16c + 4lh + jj/4 (+8), 8-byte granule 8dt + 4(G4&1) + (jj&3) of the row
-          const uint8_t* pa = vl + vlane + (16 * c) * kVRow + 64 * dt;
-          const i16x4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pa);
-          const i16x4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa + 8 * kVRow));
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(ra, rb), pb[c], o[dt], 0, 0, 0);
+          pin(o[dt]);
         }
       }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) pin(pb[c]);
+      pin(m);
+      pin(lsum);
     };
-
     // Ping-pong: waves w and w+4 share a SIMD; group 0 (w < 4) and group 1 run
     // one phase apart, so in every phase one of them issues MFMAs while the
     // other runs the softmax. For page j (LDS buffer j % 3):
@@ -347,14 +398,57 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
     //   phase 2j+1: group 0 softmax(j)       | group 1 PV(j-1) + S(j)
     // Page j+1 is copied in during phases 2j..2j+1 into the buffer page j-2 used.
     const int grp = w >> 2;
+    int64_t next_page = 0;   // table entry of the page the next even phase copies
+    // PV(j-1) then S(j) as one stream of 32 MFMAs whose LDS operands are read
+    // kAhead MFMAs early, so the reads overlap the matrix core instead of stalling it
+    auto fused = [&](auto KBc, auto VBc) {
+      constexpr int KB = decltype(KBc)::value;
+      constexpr int VB = decltype(VBc)::value;
+      const uint8_t* kl = kbuf<KB>();
+      const uint8_t* vl = vbuf<VB>();
+      constexpr int kAhead = 4;
+      auto ld = [&](int i) -> bf16x8 {
+        if (i < 16) {   // V^T, keys 16c .. 16c+15 (c = i / 4), dims 32dt .. (dt = i % 4)
+          const uint8_t* pa = vl + vofs[i & 3] + (16 * (i >> 2)) * kRowBytes;
+          const i16x4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pa);
+          const i16x4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa + 8 * kRowBytes));
+          return join(ra, rb);
+        }
+        const int ks = (i - 16) >> 1, kt = i & 1;   // K, dims 16ks .., keys 32kt ..
+        return *reinterpret_cast<const bf16x8*>(kl + kofs[ks] + kt * 32 * kRowBytes);
+      };
+      bf16x8 buf[kAhead];
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) buf[i] = ld(i);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const bf16x8 av = buf[i % kAhead];
+        if (i + kAhead < 32) buf[i % kAhead] = ld(i + kAhead);
+        if (i < 16) o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[i >> 2], o[i & 3], 0, 0, 0);
+        else st[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[(i - 16) >> 1], st[i & 1], 0, 0, 0);
+      }
+      fused_order<kAhead>();
+    };
+    // j == 0 multiplies the zero weights pb by finite V rows (buffer filled before
+    // the loop); j == npages computes scores of copied fill rows that are never used
     auto mfma_phase = [&](auto KBc, auto VBc, int j) {
-      if (j >= 1 && j - 1 < npages) pv(VBc);
-      if (j < npages) qk(KBc, j);
+      if (j <= npages) {
+        fused(KBc, VBc);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) pin(o[dt]);
+        pin(st[0]);
+        pin(st[1]);
+      }
     };
     auto phase_even = [&](auto KBc, auto VBc, auto NBc, int j) {
       wait_vmcnt<0>();        // page j's copies (issued two phases ago) are in LDS
       page_barrier();
-      fetch(NBc, j + 1);
+      fetch(NBc, j + 1, next_page);
+      next_page = page_of(j + 2);   // read now, used by the next even phase
       if (grp == 0) mfma_phase(KBc, VBc, j);
       else if (j >= 1 && j - 1 < npages) softmax(j - 1);
     };
@@ -364,7 +458,13 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
       else mfma_phase(KBc, VBc, j);
     };
 
-    fetch(Buf<0>{}, 0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[c][i] = (__bf16)0.0f;
+    fetch(Buf<0>{}, 0, page_of(0));
+    fetch(Buf<2>{}, npages, -1);   // finite rows for the zero-weight PV of the first phase
+    next_page = page_of(1);
     for (int j = 0; j <= npages; j += 3) {
       phase_even(Buf<0>{}, Buf<2>{}, Buf<1>{}, j);
       phase_odd(Buf<0>{}, Buf<2>{}, j);
