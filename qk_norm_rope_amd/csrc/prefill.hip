@@ -358,24 +358,19 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
       const float mn = need ? mx : m;
       const float corr = need ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
       const float ms = (mn == -INFINITY) ? 0.f : mn;
+      // four partial sums keep the additions independent
+      float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
 #pragma unroll
         for (int ii = 0; ii < 8; ++ii) {
           const int rg = 4 * (2 * (c & 1) + (ii >> 2)) + (ii & 3);
-          pb[c][ii] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][rg], sc, -ms));
+          const float ev = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][rg], sc, -ms));
+          ps4[ii & 3] += ev;
+          pb[c][ii] = (__bf16)ev;
         }
       }
-      // the normaliser sums the bfloat16 weights that enter P.V (two per dot2)
-      float ps = 0.f;
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int ii = 0; ii < 8; ii += 2) {
-          const bf16x2 pr = {pb[c][ii], pb[c][ii + 1]};
-          ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
-        }
+      const float ps = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
       lsum = lsum * corr + ps;
       m = mn;
       if (__any(need)) {
@@ -407,6 +402,12 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
       const uint8_t* kl = kbuf<KB>();
       const uint8_t* vl = vbuf<VB>();
       constexpr int kAhead = 4;
+      // opaque per phase: keeps the compiler from hoisting one address register per
+      // (buffer, read) out of the loop; the reads use immediate offsets instead
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pin(vofs[i]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pin(kofs[i]);
       auto ld = [&](int i) -> bf16x8 {
         if (i < 16) {   // V^T, keys 16c .. 16c+15 (c = i / 4), dims 32dt .. (dt = i % 4)
           const uint8_t* pa = vl + vofs[i & 3] + (16 * (i >> 2)) * kRowBytes;
