@@ -258,16 +258,19 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
   const int crow0 = 8 * w + (l >> 4);
   const int cslot = l & 15;
 
+  // lane l holds token l of the tile; runs are found with ballots and a wave max
+  const int my_row = sRow[l];
+  const int my_pos = sPos[l];
   int a = 0;
   while (a < kTile) {
-    const int r = uniform(sRow[a]);
-    int e = a + 1;
-    while (e < kTile && sRow[e] == r) ++e;
-    e = uniform(e);
+    const int r = __builtin_amdgcn_readlane(my_row, a);
+    const unsigned long long other = __ballot(l > a && my_row != r);
+    const int e = other ? (int)__builtin_ctzll(other) : kTile;
     if (r < 0) { a = e; continue; }
-    int maxp = 0;
-    for (int i = a; i < e; ++i) maxp = max(maxp, sPos[i]);
-    maxp = uniform(maxp);
+    int mp = (l >= a && l < e) ? my_pos : 0;
+#pragma unroll
+    for (int mm = 32; mm >= 1; mm >>= 1) mp = max(mp, __shfl_xor(mp, mm));
+    const int maxp = uniform(mp);
     const int npages = maxp / kPageSize + 1;
     const int* trow = P.table + (int64_t)r * P.pages_per_row;
     bool bad = false;
