@@ -84,6 +84,7 @@ __device__ __forceinline__ int owner(long long u, long long U, int G) {
   return i;
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 struct PageRegs {
   bf16x8 k[4];
   uint4 v[4];
@@ -170,12 +171,13 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(DecodeParams P) 
     const int pe = p0 + (int)(stop - u);
     const bool whole = (p0 == 0) && (pe == np);
 
-    // query operand: rows 0..3 = heads 4g..4g+3; k-slot 8*G4+i of step st = dim 32*G4+8*st+i
+    // query operand: rows 0..3 = heads 4g..4g+3; k-slot 8*G4+i of step st = dim 8*(4*st+G4)+i,
+    // so each K load of a step reads 64 contiguous bytes of every row
     bf16x8 qa[4];
     if (hr < kGroup) {
-      const uint16_t* qp = P.q + ((int64_t)b * n_q + g * kGroup + hr) * kHeadDim + 32 * G4;
+      const uint16_t* qp = P.q + ((int64_t)b * n_q + g * kGroup + hr) * kHeadDim;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const bf16x8*>(qp + 8 * st);
+      for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const bf16x8*>(qp + 8 * (4 * st + G4));
     } else {
 #pragma unroll
       for (int st = 0; st < 4; ++st)
@@ -199,12 +201,16 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(DecodeParams P) 
       const int64_t page = trow[p];
       r.ok = page >= 0 && page < P.num_pages;
       const int64_t pg = r.ok ? page : 0;
-      const uint16_t* krow = kbase + (pg * kPageSize + 16 * w + hr) * kHeadDim + 32 * G4;
+      const uint16_t* krow = kbase + (pg * kPageSize + 16 * w + hr) * kHeadDim + 8 * G4;
       const uint16_t* vrow = vbase + (pg * kPageSize + 16 * w + 4 * G4) * kHeadDim + 8 * hr;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) r.k[st] = *reinterpret_cast<const bf16x8*>(krow + 8 * st);
+      for (int st = 0; st < 4; ++st) r.k[st] = *reinterpret_cast<const bf16x8*>(krow + 32 * st);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) r.v[jj] = *reinterpret_cast<const uint4*>(vrow + jj * kHeadDim);
+      for (int jj = 0; jj < 4; ++jj) {
+        // V rows are read whole and once: streaming (non-temporal) loads
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vrow + jj * kHeadDim));
+        r.v[jj] = make_uint4(x[0], x[1], x[2], x[3]);
+      }
     };
 
     auto compute = [&](int p, const PageRegs& r) {
