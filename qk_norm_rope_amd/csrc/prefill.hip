@@ -7,21 +7,25 @@
 // fantasma "src/inference/model.zig", fullAttentionForward: query head h reads KV
 // head h / 4; max-subtracted softmax; weighted sum of V.
 //
-// Work item = (64-token tile of the pack, KV head g); wave w is query head 4g+w,
-// so the 4 waves share every K/V page staged in LDS. Per 64-key page and wave:
-//   S^T (64 keys x 64 queries) = K . Q^T   : 32 x v_mfma_f32_32x32x16_bf16,
+// Work item = (64-token tile of the pack, KV head g), one workgroup of 8 waves:
+// wave w is query head 4g + (w & 3) for the queries 32*(w >> 2) .. +31 of the
+// tile, so one K/V page staged in LDS feeds all 256 query rows. Per 64-key page
+// and wave:
+//   S^T (64 keys x 32 queries) = K . Q^T   : 16 x v_mfma_f32_32x32x16_bf16,
 //       K from LDS (16-byte reads), Q kept in registers;
 //   online softmax along the lane's own keys (each lane holds one query's keys,
-//       the other half sits in lane l^32), the running max only moves when the
+//       the other half sits in lane l ^ 32); the running max only moves when the
 //       page's max exceeds it by more than 2^8 (exact after the final division);
-//   O^T (128 dims x 64 queries) += V^T . P^T : 32 MFMAs, V^T read from the
+//   O^T (128 dims x 32 queries) += V^T . P^T : 16 MFMAs, V^T read from the
 //       row-major V page with ds_read_b64_tr_b16, P^T straight from the S^T
 //       accumulators (keys permuted the same way on both operands).
-// Pages stream through a double-buffered LDS stage. A tile that holds tokens of
-// several rows runs once per row ("run"); masking uses each token's position.
-// A plan kernel orders tiles by decreasing cost (largest visible position) so
-// the long ones start first; item i maps to KV head i % 8, which keeps one KV
-// head's pages on one XCD's L2.
+// Pages reach three LDS buffers through 16-byte LDS-direct buffer loads with an
+// XOR-swizzled layout. Waves w and w + 4 share a SIMD and run half a page apart:
+// in each phase one issues the MFMAs of PV(j-1) and S(j) while the other runs the
+// softmax. A tile that holds tokens of several rows runs once per row ("run");
+// masking uses each token's position. A plan kernel orders tiles by decreasing
+// cost (largest visible position) so the long ones start first; item i maps to KV
+// head i % 8, which keeps one KV head's pages on one XCD's L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -101,8 +105,6 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Marks x as produced at this point. The page loop's barriers order memory only,
 // so without this the compiler may sink a phase's register-only work (softmax,
