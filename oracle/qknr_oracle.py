@@ -78,11 +78,13 @@ def bf16_bits_from_f32(x) -> np.ndarray:
 
 
 def widen(a, dtype: str) -> np.ndarray:
-    """Stored values (float32 array, or bfloat16 bits) as float64."""
+    """Stored values (float32 array, bfloat16 bits, or float64) as float64."""
     if dtype == "bf16":
         return f32_from_bf16_bits(a).astype(np.float64)
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "f64":   # exact float64 inputs (brute-force checks)
+        return np.asarray(a, dtype=np.float64)
     raise ValueError(dtype)
 
 
@@ -313,6 +315,44 @@ def prefill(q_out, q_dtype, k_pool, v_pool, pool_dtype, table, rows, positions, 
     """Paged prefill (nest attention.linnet, prefill_paged): token p reads table[rows[p]]."""
     return attention(q_out, q_dtype, k_pool, v_pool, pool_dtype, table, rows,
                      positions, scale, **kw)
+
+
+def packed(q_out, q_dtype: str, k_rows, v_rows, kv_dtype: str, segments, positions,
+           scale: float, n_q_heads: int = NUM_Q_HEADS, n_kv_heads: int = NUM_KV_HEADS,
+           head_dim: int = HEAD_DIM, tokens=None, return_weights: bool = False):
+    """Prompts packed end to end attending only among themselves, float64.
+
+    nest attention.linnet, ``prefill_packed`` and its training form ``packed``:
+    token i attends with query head h over the pass's own tokens j that pass the
+    mask ``own[i, j] = segments[i] == segments[j] and positions[j] <= positions[i]``,
+    using the pass's keys and values ``k_rows`` / ``v_rows`` ([n, n_kv_heads, D]
+    as stored) rather than the cache; the visible keys are taken in pack order.
+    Returns out [len(tokens), n_q_heads*D] (and per-token weights if asked).
+    """
+    D = head_dim
+    group = n_q_heads // n_kv_heads
+    seg = np.asarray(segments)
+    pos = np.asarray(positions)
+    K = widen(k_rows, kv_dtype)
+    V = widen(v_rows, kv_dtype)
+    if tokens is None:
+        tokens = range(len(pos))
+    tokens = list(tokens)
+    out = np.zeros((len(tokens), n_q_heads * D), dtype=np.float64)
+    weights = []
+    for i, t in enumerate(tokens):
+        vis = np.nonzero((seg == seg[t]) & (pos <= pos[t]))[0]
+        q = widen(q_out[t], q_dtype).reshape(n_q_heads, D)
+        wt = []
+        for g in range(n_kv_heads):
+            o, w = attend(q[g * group:(g + 1) * group], K[vis, g], V[vis, g], scale)
+            out[i, g * group * D:(g + 1) * group * D] = o.reshape(-1)
+            wt.append(w)
+        if return_weights:
+            weights.append(np.concatenate(wt, axis=0))
+    if return_weights:
+        return out, weights
+    return out
 
 
 def step(q, k, v, in_dtype, pool_dtype, q_gain, k_gain, k_pool, v_pool, table,

@@ -380,6 +380,88 @@ def test_segment_mask_equals_paged_rows():
     np.testing.assert_allclose(paged, ref, rtol=1e-12, atol=1e-12)
 
 
+def _packed_case(rng, lens, firsts, seg_ids, dtype="f32"):
+    seg = np.concatenate([np.full(n, s) for s, n in zip(seg_ids, lens)])
+    pos = np.concatenate([np.arange(f, f + n) for f, n in zip(firsts, lens)])
+    P = len(seg)
+    k = rng.standard_normal((P, 8, 128)).astype(np.float32)
+    v = rng.standard_normal((P, 8, 128)).astype(np.float32)
+    q = rng.standard_normal((P, 32 * 128)).astype(np.float32)
+    if dtype == "bf16":
+        k, v, q = O.bf16_bits_from_f32(k), O.bf16_bits_from_f32(v), O.bf16_bits_from_f32(q)
+    return seg, pos, q, k, v
+
+
+def test_packed_matches_sdpa_with_own_mask():
+    # nest attention.linnet prefill_packed / packed: own[i, j] = same segment and
+    # positions[j] <= positions[i], over the pass's own keys; segment ids need not
+    # be ordered and a prompt may start past position 0 (its history is not seen)
+    rng = _rng(16)
+    seg, pos, q, k, v = _packed_case(rng, [40, 90, 30], [0, 300, 7], [7, 2, 5])
+    P = len(seg)
+    got = O.packed(q, "f32", k, v, "f32", seg, pos, W.SCALE)
+    Q = torch.from_numpy(q.reshape(P, 32, 128).transpose(1, 0, 2).copy()).double()
+    K = torch.from_numpy(k.transpose(1, 0, 2).copy()).double().repeat_interleave(4, dim=0)
+    V = torch.from_numpy(v.transpose(1, 0, 2).copy()).double().repeat_interleave(4, dim=0)
+    own = torch.from_numpy((seg[:, None] == seg[None, :]) & (pos[None, :] <= pos[:, None]))
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=own, scale=W.SCALE)
+    ref = ref.permute(1, 0, 2).reshape(P, -1).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_packed_brute_force_tiny():
+    # pure-Python loops with math.exp at Hq=4, Hkv=2, D=8
+    rng = _rng(17)
+    seg = np.array([3, 3, 3, 1, 1, 4, 4, 4, 4])
+    pos = np.array([5, 6, 7, 0, 1, 2, 3, 4, 5])
+    n, hq, hk, d = len(seg), 4, 2, 8
+    q = rng.standard_normal((n, hq * d))
+    k = rng.standard_normal((n, hk, d))
+    v = rng.standard_normal((n, hk, d))
+    got = O.packed(q, "f64", k, v, "f64", seg, pos, 0.3, n_q_heads=hq, n_kv_heads=hk, head_dim=d)
+    for i in range(n):
+        for h in range(hq):
+            g = h // (hq // hk)
+            js = [j for j in range(n) if seg[j] == seg[i] and pos[j] <= pos[i]]
+            sc = [0.3 * sum(q[i, h * d + e] * k[j, g, e] for e in range(d)) for j in js]
+            mx = max(sc)
+            ex = [math.exp(x - mx) for x in sc]
+            tot = sum(ex)
+            for e in range(d):
+                ref = sum(ex[a] * v[j, g, e] for a, j in enumerate(js)) / tot
+                assert abs(got[i, h * d + e] - ref) < 1e-12
+
+
+def test_packed_equals_paged_when_prompts_start_at_zero_bitwise():
+    # every prompt at positions 0.. on private pages: the packed form and the
+    # paged form see the same keys in the same order
+    rng = _rng(18)
+    seg, pos, q, k, v = _packed_case(rng, [70, 20, 130], [0, 0, 0], [0, 1, 2], "bf16")
+    table = np.array([[4, 0, 9], [2, 7, 8], [1, 3, 5]], dtype=np.int32)
+    kp = np.zeros((8, 10 * 64, 128), np.uint16)
+    vp = np.zeros((8, 10 * 64, 128), np.uint16)
+    O.apply_writes(kp, vp, [O.page_slot(table[s], p) for s, p in zip(seg, pos)], k, v)
+    a = O.packed(q, "bf16", k, v, "bf16", seg, pos, W.SCALE)
+    b = O.prefill(q, "bf16", kp, vp, "bf16", table, seg, pos, W.SCALE)
+    assert np.array_equal(a, b)
+
+
+def test_packed_ignores_history_bitwise():
+    # a prompt chunk at positions 300.. attends only to itself: the same as the
+    # paged form of the same keys placed at positions 0.. of a fresh row (the
+    # mask uses positions only through their order within the prompt)
+    rng = _rng(19)
+    seg, pos, q, k, v = _packed_case(rng, [100, 50], [300, 64], [0, 1], "bf16")
+    a = O.packed(q, "bf16", k, v, "bf16", seg, pos, W.SCALE)
+    rel = np.concatenate([np.arange(100), np.arange(50)])
+    table = np.array([[0, 1], [2, 3]], dtype=np.int32)
+    kp = np.zeros((8, 4 * 64, 128), np.uint16)
+    vp = np.zeros((8, 4 * 64, 128), np.uint16)
+    O.apply_writes(kp, vp, [O.page_slot(table[s], p) for s, p in zip(seg, rel)], k, v)
+    b = O.prefill(q, "bf16", kp, vp, "bf16", table, seg, rel, W.SCALE)
+    assert np.array_equal(a, b)
+
+
 def test_step_writes_before_reads():
     # a prompt chunk sees its own keys through the pool: the first token of a
     # chunk at position 0 attends to exactly its own value
