@@ -174,6 +174,31 @@ int paged_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
 size_t paged_prefill_attn_workspace(const qkr_pool* pool, int32_t n_tokens);
 
 /*
+ * packed_prefill_attn -- prompts packed end to end that attend only among
+ * themselves (attention.linnet, prefill_packed; on a scratch pool also the
+ * training form packed, which keeps no cache).
+ *
+ * Token p (query q[p], prompt segments[p], row rows[p], position positions[p])
+ * attends with each query head over the tokens j of its own prompt with
+ * positions[j] <= positions[p]. Their keys and values are read from the pool,
+ * where qknorm_rope_append wrote them; history in the row before the prompt's
+ * first position is not seen.
+ * Preconditions (not checked on the device): every prompt is one contiguous run
+ * of the pack whose positions rise by one, and all its tokens use one row.
+ * segments: device int32 [n_tokens]; the other arguments as for
+ * paged_prefill_attn (same row-length limit for a bfloat16 pool).
+ * workspace: at least packed_prefill_attn_workspace() bytes; contents need no
+ * initialisation.
+ */
+int packed_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                        const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
+                        const int32_t* rows, const int32_t* positions, const int32_t* segments,
+                        float scale, float* out, void* workspace, size_t workspace_bytes);
+
+size_t packed_prefill_attn_workspace(const qkr_pool* pool, int32_t n_tokens);
+
+/*
  * qkr_rope_table -- host helper: the RoPE cos/sin table (host memory).
  * For pos < rope_rows and i < head_dim/2:
  *   inv = 1 / theta^(2i/head_dim), a = pos*inv (double precision),

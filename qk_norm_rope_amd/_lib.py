@@ -24,6 +24,8 @@ EXPORTED = (
     "paged_decode_attn_workspace",
     "paged_prefill_attn",
     "paged_prefill_attn_workspace",
+    "packed_prefill_attn",
+    "packed_prefill_attn_workspace",
     "qkr_rope_table",
     "qkr_status_str",
     "qkr_last_error",
@@ -72,6 +74,10 @@ def _load():
     lib.paged_prefill_attn.argtypes = [vp, pool_p, i32, vp, vp, vp, vp, i32, i32, vp, vp, f32, vp, vp, sz]
     lib.paged_prefill_attn_workspace.restype = sz
     lib.paged_prefill_attn_workspace.argtypes = [pool_p, i32]
+    lib.packed_prefill_attn.restype = ctypes.c_int
+    lib.packed_prefill_attn.argtypes = [vp, pool_p, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, f32, vp, vp, sz]
+    lib.packed_prefill_attn_workspace.restype = sz
+    lib.packed_prefill_attn_workspace.argtypes = [pool_p, i32]
     lib.qkr_rope_table.restype = ctypes.c_int
     lib.qkr_rope_table.argtypes = [ctypes.c_double, i32, i32, vp, vp]
     lib.qkr_status_str.restype = ctypes.c_char_p
@@ -220,6 +226,31 @@ def paged_prefill_attn(q, k_pool, v_pool, table, rows, positions, scale: float, 
         float(scale), _ptr(out, "out", torch.float32, n * n_q * HEAD_DIM),
         _ptr(workspace, "workspace"), ws_bytes)
     _check(st, "paged_prefill_attn")
+
+
+def packed_workspace_bytes(k_pool, num_q_heads: int, n_tokens: int) -> int:
+    pool = pool_desc(k_pool, num_q_heads)
+    return int(LIB.packed_prefill_attn_workspace(ctypes.byref(pool), int(n_tokens)))
+
+
+def packed_prefill_attn(q, k_pool, v_pool, table, rows, positions, segments, scale: float, out,
+                        workspace=None, stream=None) -> None:
+    """out[p] <- attention of token p over the tokens of its own prompt (segment) up to its position."""
+    import torch
+    n_q = q.shape[-1] // HEAD_DIM
+    pool = pool_desc(k_pool, n_q)
+    n = int(positions.numel())
+    ppr = int(table.shape[-1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = LIB.packed_prefill_attn(
+        _stream(stream), ctypes.byref(pool), n, _ptr(q, "q", k_pool.dtype, n * n_q * HEAD_DIM),
+        _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
+        _ptr(table, "table", torch.int32), int(table.shape[0]), ppr,
+        _ptr(rows, "rows", torch.int32, n), _ptr(positions, "positions", torch.int32, n),
+        _ptr(segments, "segments", torch.int32, n),
+        float(scale), _ptr(out, "out", torch.float32, n * n_q * HEAD_DIM),
+        _ptr(workspace, "workspace"), ws_bytes)
+    _check(st, "packed_prefill_attn")
 
 
 def version() -> int:

@@ -41,6 +41,47 @@ int launch_status(hipError_t e) {
   return QKR_ELAUNCH;
 }
 
+// Workspace of the packed form: the bfloat16 kernel's tile schedule, then the
+// first visible position of every token.
+size_t packed_workspace(const qkr_pool* pool, int32_t n_tokens) {
+  const size_t lo = qknr::segment_start_bytes(n_tokens);
+  if (pool->dtype != QKR_BF16) return lo;
+  return qknr::prefill_workspace_bytes(n_tokens, pool->num_kv_heads) + lo;
+}
+
+int prefill_common(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                   const void* q, const void* k_pool, const void* v_pool,
+                   const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
+                   const int32_t* rows, const int32_t* positions, const int32_t* segments,
+                   float scale, float* out, void* workspace, size_t workspace_bytes) {
+  int st = check_pool(pool);
+  if (st != QKR_OK) return st;
+  if (n_tokens < 0) return QKR_EINVAL;
+  if (n_tokens == 0) return QKR_OK;
+  if (!q || !k_pool || !v_pool || !table || !rows || !positions || !out || n_table_rows <= 0 ||
+      pages_per_row <= 0)
+    return QKR_EINVAL;
+  if (!std::isfinite(scale)) return QKR_EINVAL;
+  qknr::AttnArgs a;
+  a.n_queries = n_tokens;
+  a.n_q_heads = pool->num_q_heads;
+  a.n_kv_heads = pool->num_kv_heads;
+  a.bf16 = pool->dtype == QKR_BF16;
+  a.q = q; a.k_pool = k_pool; a.v_pool = v_pool;
+  a.num_pages = pool->num_pages;
+  a.table = table; a.n_table_rows = n_table_rows; a.pages_per_row = pages_per_row;
+  a.rows = rows; a.positions = positions; a.segments = segments;
+  a.scale = scale; a.out = out;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t need = segments ? packed_workspace(pool, n_tokens)
+                               : (a.bf16 ? qknr::prefill_workspace_bytes(n_tokens, pool->num_kv_heads) : 0);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return QKR_EWORKSPACE;
+  if (!a.bf16) return launch_status(qknr::launch_attention_generic(s, a));
+  if (pages_per_row > qknr::prefill_max_pages_per_row()) return QKR_EUNSUPPORTED;
+  return launch_status(qknr::launch_prefill_bf16(s, a));
+}
+
 }  // namespace
 
 extern "C" {
@@ -158,30 +199,25 @@ int paged_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
                        const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
                        const int32_t* rows, const int32_t* positions,
                        float scale, float* out, void* workspace, size_t workspace_bytes) {
-  int st = check_pool(pool);
-  if (st != QKR_OK) return st;
-  if (n_tokens < 0) return QKR_EINVAL;
-  if (n_tokens == 0) return QKR_OK;
-  if (!q || !k_pool || !v_pool || !table || !rows || !positions || !out || n_table_rows <= 0 ||
-      pages_per_row <= 0)
-    return QKR_EINVAL;
-  if (!std::isfinite(scale)) return QKR_EINVAL;
-  qknr::AttnArgs a;
-  a.n_queries = n_tokens;
-  a.n_q_heads = pool->num_q_heads;
-  a.n_kv_heads = pool->num_kv_heads;
-  a.bf16 = pool->dtype == QKR_BF16;
-  a.q = q; a.k_pool = k_pool; a.v_pool = v_pool;
-  a.num_pages = pool->num_pages;
-  a.table = table; a.n_table_rows = n_table_rows; a.pages_per_row = pages_per_row;
-  a.rows = rows; a.positions = positions; a.scale = scale; a.out = out;
-  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!a.bf16) return launch_status(qknr::launch_attention_generic(s, a));
-  if (pages_per_row > qknr::prefill_max_pages_per_row()) return QKR_EUNSUPPORTED;
-  const size_t need = qknr::prefill_workspace_bytes(n_tokens, pool->num_kv_heads);
-  if (!workspace || workspace_bytes < need) return QKR_EWORKSPACE;
-  return launch_status(qknr::launch_prefill_bf16(s, a));
+  return prefill_common(stream, pool, n_tokens, q, k_pool, v_pool, table, n_table_rows,
+                        pages_per_row, rows, positions, nullptr, scale, out, workspace,
+                        workspace_bytes);
+}
+
+size_t packed_prefill_attn_workspace(const qkr_pool* pool, int32_t n_tokens) {
+  if (check_pool(pool) != QKR_OK || n_tokens <= 0) return 0;
+  return packed_workspace(pool, n_tokens);
+}
+
+int packed_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                        const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
+                        const int32_t* rows, const int32_t* positions, const int32_t* segments,
+                        float scale, float* out, void* workspace, size_t workspace_bytes) {
+  if (!segments && n_tokens > 0) return QKR_EINVAL;
+  return prefill_common(stream, pool, n_tokens, q, k_pool, v_pool, table, n_table_rows,
+                        pages_per_row, rows, positions, segments, scale, out, workspace,
+                        workspace_bytes);
 }
 
 }  // extern "C"

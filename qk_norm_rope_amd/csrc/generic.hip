@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void attention_generic_kernel(
     int n_q_heads, const T* __restrict__ q, const T* __restrict__ k_pool,
     const T* __restrict__ v_pool, int64_t num_pages, const int* __restrict__ table,
     int n_table_rows, int pages_per_row, const int* __restrict__ rows,
-    const int* __restrict__ positions, float scale, float* __restrict__ out) {
+    const int* __restrict__ positions, const int* __restrict__ lo, float scale, float* __restrict__ out) {
   const int t = blockIdx.x;
   const int g = blockIdx.y;
   const int w = threadIdx.x >> 6;
@@ -49,7 +49,8 @@ __global__ __launch_bounds__(256) void attention_generic_kernel(
   const T* vb = v_pool + (int64_t)g * pool_slots * kHeadDim + 2 * lane;
   const int* trow = table + (int64_t)row * pages_per_row;
   float m = -INFINITY, l = 0.f, a0 = 0.f, a1 = 0.f;
-  for (int j = 0; j <= pos; ++j) {
+  const int first = lo ? min(max(lo[t], 0), pos) : 0;   // packed form: own segment only
+  for (int j = first; j <= pos; ++j) {
     const int64_t page = trow[j / kPageSize];
     if (page < 0 || page >= num_pages) continue;
     const int64_t slot = page * kPageSize + j % kPageSize;
@@ -73,16 +74,22 @@ __global__ __launch_bounds__(256) void attention_generic_kernel(
 
 hipError_t launch_attention_generic(hipStream_t stream, const AttnArgs& a) {
   const dim3 grid(a.n_queries, a.n_kv_heads), block(256);
+  int32_t* lo = nullptr;
+  if (a.segments) {
+    lo = static_cast<int32_t*>(a.workspace);
+    const hipError_t e = launch_segment_start(stream, a.n_queries, a.positions, a.segments, lo);
+    if (e != hipSuccess) return e;
+  }
   if (a.bf16) {
     hipLaunchKernelGGL(attention_generic_kernel<uint16_t>, grid, block, 0, stream, a.n_q_heads,
                        (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,
                        a.num_pages, a.table, a.n_table_rows, a.pages_per_row, a.rows,
-                       a.positions, a.scale, a.out);
+                       a.positions, lo, a.scale, a.out);
   } else {
     hipLaunchKernelGGL(attention_generic_kernel<float>, grid, block, 0, stream, a.n_q_heads,
                        (const float*)a.q, (const float*)a.k_pool, (const float*)a.v_pool,
                        a.num_pages, a.table, a.n_table_rows, a.pages_per_row, a.rows,
-                       a.positions, a.scale, a.out);
+                       a.positions, lo, a.scale, a.out);
   }
   return hipGetLastError();
 }

@@ -34,6 +34,7 @@ struct AttnArgs {
   int n_table_rows, pages_per_row;
   const int32_t* rows;    // prefill: row of each token; decode: nullptr (row = index)
   const int32_t* positions;
+  const int32_t* segments = nullptr;   // packed prefill: prompt of each token, else nullptr
   float scale;
   float* out;
   void* workspace;
@@ -50,9 +51,18 @@ hipError_t launch_decode_bf16(hipStream_t stream, const AttnArgs& a);
 // Prefill: MFMA flash attention over 64-token tiles of the pack.
 size_t prefill_workspace_bytes(int n_tokens, int n_kv_heads);
 int prefill_max_pages_per_row();
+// With a.segments set, the workspace continues after prefill_workspace_bytes with
+// segment_start_bytes of first visible positions.
 hipError_t launch_prefill_bf16(hipStream_t stream, const AttnArgs& a);
 
-// One workgroup per (query, KV head); any pool dtype. Used for float32 pools.
+// Packed form: first visible position of every token (its segment's first position).
+size_t segment_start_bytes(int n_tokens);
+hipError_t launch_segment_start(hipStream_t stream, int n_tokens, const int32_t* positions,
+                                const int32_t* segments, int32_t* lo);
+
+// One workgroup per (query, KV head); any pool dtype. Used for float32 pools. With
+// a.segments set, the first segment_start_bytes of the workspace take the first
+// visible positions.
 hipError_t launch_attention_generic(hipStream_t stream, const AttnArgs& a);
 
 }  // namespace qknr

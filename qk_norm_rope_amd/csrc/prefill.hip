@@ -43,19 +43,26 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // ---------------------------------------------------------------- planning
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(int n_tokens, const int* __restrict__ positions,
-                                                            int n_tiles, int* __restrict__ order) {
+                                                            const int* __restrict__ lo, int n_tiles,
+                                                            int* __restrict__ order) {
   __shared__ unsigned long long keys[kPlanMaxTiles];
   int npow2 = 1;
   while (npow2 < n_tiles) npow2 <<= 1;
-  // cost of a tile: its largest visible position + 1; one wave per tile, one lane per token
+  // cost of a tile: keys from its smallest first visible position to its largest
+  // position; one wave per tile, one lane per token
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n_waves = blockDim.x >> 6;
   for (int i = wave; i < npow2; i += n_waves) {
     int cost = 0;
     if (i < n_tiles) {
       const int t = i * kTile + lane;
-      cost = t < n_tokens ? max(positions[t] + 1, 0) : 0;
+      int hi = t < n_tokens ? max(positions[t] + 1, 0) : 0;
+      int first = (t < n_tokens && lo) ? max(lo[t], 0) : (lo ? 0x7fffffff : 0);
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) cost = max(cost, __shfl_xor(cost, m));
+      for (int m = 32; m >= 1; m >>= 1) {
+        hi = max(hi, __shfl_xor(hi, m));
+        first = min(first, __shfl_xor(first, m));
+      }
+      cost = max(hi - first, 0);
     }
     if (lane == 0)
       keys[i] = i < n_tiles ? ((unsigned long long)(0xffffffffu - (unsigned)cost) << 32) | (unsigned)i : ~0ull;
@@ -77,6 +84,37 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(int n_tokens, const 
   for (int i = threadIdx.x; i < n_tiles; i += blockDim.x) order[i] = (int)(keys[i] & 0xffffffffu);
 }
 
+// First visible position of every token of a pack whose prompts attend only among
+// themselves (nest "models/qwen3-8b/files", src/attention.linnet prefill_packed:
+// token i sees token j when segments agree and positions[j] <= positions[i]). Each
+// segment is one run of the pack with positions rising by one, so the first visible
+// position is the position of the run's first token. One workgroup: a chunk of
+// tokens per thread, run starts carried across chunks by a prefix max.
+__global__ __launch_bounds__(1024) void segment_start_kernel(int n_tokens, const int* __restrict__ positions,
+                                                             const int* __restrict__ segments,
+                                                             int* __restrict__ lo) {
+  __shared__ int s_last[1024];
+  const int tid = threadIdx.x;
+  const int per = (n_tokens + 1023) / 1024;
+  const int c0 = min(tid * per, n_tokens), c1 = min(c0 + per, n_tokens);
+  int last = -1;   // index of the last run start inside this chunk
+  for (int i = c0; i < c1; ++i)
+    if (i == 0 || segments[i] != segments[i - 1]) last = i;
+  s_last[tid] = last;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {   // inclusive prefix max (Hillis-Steele)
+    const int x = tid >= d ? s_last[tid - d] : -1;
+    __syncthreads();
+    s_last[tid] = max(s_last[tid], x);
+    __syncthreads();
+  }
+  int start = tid > 0 ? s_last[tid - 1] : -1;
+  for (int i = c0; i < c1; ++i) {
+    if (i == 0 || segments[i] != segments[i - 1]) start = i;
+    lo[i] = min(positions[start], positions[i]);
+  }
+}
+
 // ---------------------------------------------------------------- attention
 struct PrefillParams {
   int n_tokens, n_kv;
@@ -91,6 +129,7 @@ struct PrefillParams {
   float scale_log2;
   float* out;
   const int* order;
+  const int* lo;   // first visible position per token (packed form), or null (0)
 };
 
 __device__ __forceinline__ bf16x8 join(i16x4 a, i16x4 b) {
@@ -191,7 +230,7 @@ __device__ __forceinline__ void page_barrier() {
 // from HBM into LDS (global_load_lds) one page ahead of the computation.
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void paged_prefill_bf16_kernel(PrefillParams P) {
-  __shared__ int sRow[kTile], sPos[kTile];
+  __shared__ int sRow[kTile], sPos[kTile], sLo[kTile];
   __shared__ int sTab[kTabCache];
 
   const int n_q = P.n_kv * kGroup;
@@ -210,19 +249,22 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
 
   if (tid < kTile) {
     const int t = t0 + tid;
-    int r = -1, p = -1;
+    int r = -1, p = -1, f = 0;
     if (t < P.n_tokens) {
       r = P.rows[t];
       p = P.positions[t];
       if (r < 0 || r >= P.n_table_rows || p < 0 || p >= max_pos) r = -1;
+      if (P.lo) f = min(max(P.lo[t], 0), max(p, 0));
     }
     sRow[tid] = r;
     sPos[tid] = p;
+    sLo[tid] = f;
   }
   __syncthreads();
 
   // Q^T operand: lane holds query qn, dims 16*ks + 8*lh .. +7
   const int qpos = sPos[qn];
+  const int qlo = sLo[qn];   // first visible position of the lane's query
   bf16x8 qb[8];
   {
     const int t = t0 + qn;
@@ -263,6 +305,7 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
   // lane l holds token l of the tile; runs are found with ballots and a wave max
   const int my_row = sRow[l];
   const int my_pos = sPos[l];
+  const int my_lo = sLo[l];
   int a = 0;
   while (a < kTile) {
     const int r = __builtin_amdgcn_readlane(my_row, a);
@@ -270,9 +313,14 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
     const int e = other ? (int)__builtin_ctzll(other) : kTile;
     if (r < 0) { a = e; continue; }
     int mp = (l >= a && l < e) ? my_pos : 0;
+    int mf = (l >= a && l < e) ? my_lo : 0x7fffffff;
 #pragma unroll
-    for (int mm = 32; mm >= 1; mm >>= 1) mp = max(mp, __shfl_xor(mp, mm));
+    for (int mm = 32; mm >= 1; mm >>= 1) {
+      mp = max(mp, __shfl_xor(mp, mm));
+      mf = min(mf, __shfl_xor(mf, mm));
+    }
     const int maxp = uniform(mp);
+    const int j0 = uniform(mf) / kPageSize;   // first page any query of the run sees
     const int npages = maxp / kPageSize + 1;
     const int* trow = P.table + (int64_t)r * P.pages_per_row;
     bool bad = false;
@@ -295,9 +343,15 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
     const bool active = qn >= a && qn < e;
     // smallest position among the wave's queries; -1 when some query is not in this run
     int wmin = active ? qpos : -1;
+    // largest first visible position among the wave's queries of this run
+    int wlo = active ? qlo : 0;
 #pragma unroll
-    for (int mm = 32; mm >= 1; mm >>= 1) wmin = min(wmin, __shfl_xor(wmin, mm));
+    for (int mm = 32; mm >= 1; mm >>= 1) {
+      wmin = min(wmin, __shfl_xor(wmin, mm));
+      wlo = max(wlo, __shfl_xor(wlo, mm));
+    }
     wmin = uniform(wmin);
+    wlo = uniform(wlo);
 
     float m = -INFINITY;
     float lsum = 0.f;
@@ -339,14 +393,17 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
     auto softmax = [&](int j) {
       const bool pok = !any_bad || page_ok(uniform64(page_of(j)));
       const int kpos0 = j * kPageSize;
-      if (!pok || wmin < kpos0 + kPageSize - 1) {
+      if (!pok || wmin < kpos0 + kPageSize - 1 || wlo > kpos0) {
         // key index = kt*32 + 8*(rg>>2) + 4*lh + (rg&3); compare the constant part
         const int lim = ((active && pok) ? qpos - kpos0 : -1) - 4 * lh;
+        const int low = qlo - kpos0 - 4 * lh;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int rg = 0; rg < 16; ++rg)
-            st[kt][rg] = (kt * 32 + 8 * (rg >> 2) + (rg & 3) <= lim) ? st[kt][rg] : -INFINITY;
+          for (int rg = 0; rg < 16; ++rg) {
+            const int kk = kt * 32 + 8 * (rg >> 2) + (rg & 3);
+            st[kt][rg] = (kk <= lim && kk >= low) ? st[kt][rg] : -INFINITY;
+          }
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -393,11 +450,13 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
     };
     // Ping-pong: waves w and w+4 share a SIMD; group 0 (w < 4) and group 1 run
     // one phase apart, so in every phase one of them issues MFMAs while the
-    // other runs the softmax. For page j (LDS buffer j % 3):
+    // other runs the softmax. For page j0 + j (j counted from the run's first
+    // visible page j0; LDS buffer j % 3):
     //   phase 2j  : group 0 PV(j-1) + S(j)   | group 1 softmax(j-1)
     //   phase 2j+1: group 0 softmax(j)       | group 1 PV(j-1) + S(j)
     // Page j+1 is copied in during phases 2j..2j+1 into the buffer page j-2 used.
     const int grp = w >> 2;
+    const int nrel = npages - j0;   // pages of the run from its first visible one
     int64_t next_page = 0;   // table entry of the page the next even phase copies
     // PV(j-1) then S(j) as one stream of 32 MFMAs whose LDS operands are read
     // kAhead MFMAs early, so the reads overlap the matrix core instead of stalling it
@@ -440,9 +499,9 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
       fused_order<kAhead>();
     };
     // j == 0 multiplies the zero weights pb by finite V rows (buffer filled before
-    // the loop); j == npages computes scores of copied fill rows that are never used
+    // the loop); j == nrel computes scores of copied fill rows that are never used
     auto mfma_phase = [&](auto KBc, auto VBc, int j) {
-      if (j <= npages) {
+      if (j <= nrel) {
         fused(KBc, VBc);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) pin(o[dt]);
@@ -453,14 +512,14 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
     auto phase_even = [&](auto KBc, auto VBc, auto NBc, int j) {
       wait_vmcnt<0>();        // page j's copies (issued two phases ago) are in LDS
       page_barrier();
-      fetch(NBc, j + 1, next_page);
-      next_page = page_of(j + 2);   // read now, used by the next even phase
+      fetch(NBc, j0 + j + 1, next_page);
+      next_page = page_of(j0 + j + 2);   // read now, used by the next even phase
       if (grp == 0) mfma_phase(KBc, VBc, j);
-      else if (j >= 1 && j - 1 < npages) softmax(j - 1);
+      else if (j >= 1 && j - 1 < nrel) softmax(j0 + j - 1);
     };
     auto phase_odd = [&](auto KBc, auto VBc, int j) {
       page_barrier();
-      if (grp == 0) { if (j < npages) softmax(j); }
+      if (grp == 0) { if (j < nrel) softmax(j0 + j); }
       else mfma_phase(KBc, VBc, j);
     };
 
@@ -468,10 +527,10 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[c][i] = (__bf16)0.0f;
-    fetch(Buf<0>{}, 0, page_of(0));
+    fetch(Buf<0>{}, j0, page_of(j0));
     fetch(Buf<2>{}, npages, -1);   // finite rows for the zero-weight PV of the first phase
-    next_page = page_of(1);
-    for (int j = 0; j <= npages; j += 3) {
+    next_page = page_of(j0 + 1);
+    for (int j = 0; j <= nrel; j += 3) {
       phase_even(Buf<0>{}, Buf<2>{}, Buf<1>{}, j);
       phase_odd(Buf<0>{}, Buf<2>{}, j);
       phase_even(Buf<1>{}, Buf<0>{}, Buf<2>{}, j + 1);
@@ -510,13 +569,27 @@ size_t prefill_workspace_bytes(int n_tokens, int /*n_kv_heads*/) {
   return (tiles * sizeof(int) + 255) / 256 * 256;
 }
 
+size_t segment_start_bytes(int n_tokens) { return ((size_t)n_tokens * sizeof(int) + 255) / 256 * 256; }
+
+hipError_t launch_segment_start(hipStream_t stream, int n_tokens, const int32_t* positions,
+                                const int32_t* segments, int32_t* lo) {
+  hipLaunchKernelGGL(segment_start_kernel, dim3(1), dim3(1024), 0, stream, n_tokens, positions, segments, lo);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_bf16(hipStream_t stream, const AttnArgs& a) {
   const int n_tiles = (a.n_queries + kTile - 1) / kTile;
   int* order = nullptr;
+  int* lo = nullptr;
+  if (a.segments) {   // packed form: first visible positions after the tile order
+    lo = reinterpret_cast<int*>(static_cast<char*>(a.workspace) + prefill_workspace_bytes(a.n_queries, a.n_kv_heads));
+    hipError_t e = launch_segment_start(stream, a.n_queries, a.positions, a.segments, lo);
+    if (e != hipSuccess) return e;
+  }
   if (n_tiles <= kPlanMaxTiles) {
     order = static_cast<int*>(a.workspace);
     hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, a.n_queries,
-                       a.positions, n_tiles, order);
+                       a.positions, lo, n_tiles, order);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -535,6 +608,7 @@ hipError_t launch_prefill_bf16(hipStream_t stream, const AttnArgs& a) {
   P.scale_log2 = a.scale * kLog2e;
   P.out = a.out;
   P.order = order;
+  P.lo = lo;
   hipLaunchKernelGGL(paged_prefill_bf16_kernel, dim3(n_tiles * a.n_kv_heads), dim3(512), 0, stream, P);
   return hipGetLastError();
 }
