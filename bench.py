@@ -64,6 +64,39 @@ def algorithmic_work(w):
             "prefill_pairs": pre_pairs, "append_bytes": app_bytes}
 
 
+def measure_packed(Q, W, w, t, q_out, k_pool, v_pool, out, stream, reps=10):
+    """The step's prompt tokens through packed_prefill_attn (each chunk its own
+    prompt, attending only among itself), timed after the step's timed region."""
+    import numpy as np
+    import torch
+    P = w.n_prefill
+    seg = t["rows"]   # one prompt per chunk, one row per prompt
+    ws = torch.zeros(max(1, Q.packed_workspace_bytes(k_pool, 32, P)), dtype=torch.uint8, device=out.device)
+    for _ in range(2):
+        Q.packed_prefill_attn(q_out[:P], k_pool, v_pool, t["table"], t["rows"], t["positions"], seg,
+                              W.SCALE, out, ws)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        Q.packed_prefill_attn(q_out[:P], k_pool, v_pool, t["table"], t["rows"], t["positions"], seg,
+                              W.SCALE, out, ws)
+    b.record(stream)
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    rows = w.rows.astype(np.int64)
+    pos = w.positions.astype(np.int64)
+    first = {}
+    for r, p in zip(rows, pos):
+        first[r] = min(first.get(r, p), p)
+    pairs = int(sum(p - first[r] + 1 for r, p in zip(rows, pos)))
+    flops = pairs * 4 * 128 * 32
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"tflops": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops_per_launch": flops, "ms_per_launch": round(ms, 5), "bound": "mfma",
+            "form": "each chunk attends only to itself (no history)"}
+
+
 def oracle_snapshot(w, k_pool, v_pool, sample_rows=128, prefill_tokens=256, seed=0):
     """Host copies of the pool slots the oracle sample reads, taken from the
     generator's pre-step pools before any library kernel has run."""
@@ -252,6 +285,8 @@ def main():
         times[k] /= args.steps  # ms per launch
     step_ms = sum(times.values())
 
+    packed = measure_packed(Q, W, w, t, q_out, k_pool, v_pool, pre_out, stream) if P else None
+
     work = algorithmic_work(w)
     dec_gbs = work["decode_bytes"] / (times["decode"] * 1e-3) / 1e9 if R else 0.0
     pre_tflops = work["prefill_flops"] / (times["prefill"] * 1e-3) / 1e12 if P else 0.0
@@ -287,6 +322,8 @@ def main():
                    "bytes_per_launch": work["append_bytes"], "ms_per_launch": round(times["append"], 5),
                    "bound": "hbm"},
     }
+    if packed is not None:
+        result["packed_prefill"] = packed
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, snap)
     print(json.dumps(result), flush=True)
