@@ -168,58 +168,101 @@ def rope_table(theta: float, n_pos: int, head_dim: int = HEAD_DIM):
 # fullAttentionForward (rmsNorm of each head slice with q_norm / k_norm).
 # --------------------------------------------------------------------------
 
+def _pair_sums(p) -> np.ndarray:
+    """Pairwise float32 sum along the last axis, neighbours first; an odd last
+    element is carried up a level unchanged."""
+    while p.shape[-1] > 1:
+        n = p.shape[-1]
+        m = n - n % 2
+        q = p[..., 0:m:2] + p[..., 1:m:2]
+        if n % 2:
+            q = np.concatenate([q, p[..., m:]], axis=-1)
+        p = q
+    return p[..., 0]
+
+
+def _head_square_sums(x) -> np.ndarray:
+    """Per head (last axis, width D): sum of squares by recipe steps 1-2."""
+    d = x.shape[-1]
+    half = d // 2
+    assert half & (half - 1) == 0, "head_dim/2 must be a power of two"
+    sq = x * x
+    return _pair_sums(sq[..., :half] + sq[..., half:])
+
+
 def qk_norm(x, gain, eps: float = RMS_EPS) -> np.ndarray:
     """RMS-normalise the last axis of ``x`` (float32 recipe steps 1-4)."""
     x = np.asarray(x, dtype=np.float32)
     g = np.asarray(gain, dtype=np.float32)
     d = x.shape[-1]
-    half = d // 2
-    assert half & (half - 1) == 0, "head_dim/2 must be a power of two"
-    sq = x * x
-    p = sq[..., :half] + sq[..., half:]
-    while p.shape[-1] > 1:
-        p = p[..., 0::2] + p[..., 1::2]
-    ss = p[..., 0]
+    ss = _head_square_sums(x)
     ms = ss / np.float32(d)
     r = np.float32(1.0) / np.sqrt(ms + np.float32(eps))
     return (x * r[..., None]) * g
 
 
-def rope_rotate(y, cos, sin) -> np.ndarray:
-    """Rotate pairs (i, i + D/2) by the angle whose cos/sin are given (recipe step 5).
+def qk_norm_whole(x, gain, eps: float = RMS_EPS) -> np.ndarray:
+    """RMS-normalise all heads of a token together: ``x`` [..., H, D], ``gain`` [H*D].
 
-    ``cos``/``sin`` broadcast against ``y[..., :D/2]``. fantasma ``applyRope``:
-    ``x*cos + rotate_half(x)*sin`` with ``rotate_half(x) = cat(-x2, x1)``.
+    logicaffeine ``author.rs``, ``qk_norm_segments``: with ``qk_norm_whole`` the
+    q and k norms run over one segment of width heads*head_dim (kv_heads*head_dim)
+    instead of one per head. Pinned float32 order: each head's sum of squares by
+    recipe steps 1-2, the head sums added pairwise (neighbours first, an odd last
+    one carried up), ``ms = total / (H*D)``, ``r = 1/sqrt(ms + eps)``,
+    ``y = (x*r)*g``.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    h, d = x.shape[-2], x.shape[-1]
+    g = np.asarray(gain, dtype=np.float32).reshape(h, d)
+    total = _pair_sums(_head_square_sums(x))
+    ms = total / np.float32(h * d)
+    r = np.float32(1.0) / np.sqrt(ms + np.float32(eps))
+    return (x * r[..., None, None]) * g
+
+
+def rope_rotate(y, cos, sin, rotary_dim: int | None = None) -> np.ndarray:
+    """Rotate pairs (i, i + R/2) of the first R = rotary_dim elements by the angle
+    whose cos/sin are given (recipe step 5); the other elements pass unchanged.
+
+    ``cos``/``sin`` broadcast against ``y[..., :R/2]``. fantasma ``applyRope``:
+    ``x*cos + rotate_half(x)*sin`` with ``rotate_half(x) = cat(-x2, x1)`` over the
+    first ``rotary_dim`` elements (R = D: the whole head).
     """
     y = np.asarray(y, dtype=np.float32)
-    half = y.shape[-1] // 2
+    r = y.shape[-1] if rotary_dim is None else int(rotary_dim)
+    half = r // 2
     a = y[..., :half]
-    b = y[..., half:]
+    b = y[..., half:r]
     c = np.asarray(cos, dtype=np.float32)
     s = np.asarray(sin, dtype=np.float32)
-    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+    return np.concatenate([a * c - b * s, b * c + a * s, y[..., r:]], axis=-1)
 
 
 def append(q, k, v, in_dtype: str, pool_dtype: str, q_gain, k_gain, positions,
            eps: float = RMS_EPS, theta: float = ROPE_THETA,
            n_q_heads: int = NUM_Q_HEADS, n_kv_heads: int = NUM_KV_HEADS,
-           head_dim: int = HEAD_DIM):
+           head_dim: int = HEAD_DIM, norm_whole: bool = False, rotary_dim: int | None = None):
     """QK-norm + RoPE of every token, and the values to store.
 
     ``q``: [n, n_q_heads*head_dim], ``k``/``v``: [n, n_kv_heads*head_dim], token
     major with head h at columns h*D .. h*D+D-1 (nest attention.linnet,
     split_heads). Returns ``(q_out, k_rows, v_rows)`` in the pool dtype with
     shapes [n, n_q_heads*D], [n, n_kv_heads, D], [n, n_kv_heads, D].
+    ``norm_whole``: one RMS norm over all heads (gains [n_heads*D]);
+    ``rotary_dim``: rotate only the first R elements of every head, with the
+    table of an R-wide head (``inv_freq = 1/theta^(2i/R)``).
     """
     n = len(positions)
     D = head_dim
+    R = D if rotary_dim is None else int(rotary_dim)
     qf = as_f32(q, in_dtype).reshape(n, n_q_heads, D)
     kf = as_f32(k, in_dtype).reshape(n, n_kv_heads, D)
     vf = as_f32(v, in_dtype).reshape(n, n_kv_heads, D)
-    cos = np.stack([rope_row(theta, int(p), D)[0] for p in positions]) if n else np.zeros((0, D // 2), np.float32)
-    sin = np.stack([rope_row(theta, int(p), D)[1] for p in positions]) if n else np.zeros((0, D // 2), np.float32)
-    qn = rope_rotate(qk_norm(qf, q_gain, eps), cos[:, None, :], sin[:, None, :])
-    kn = rope_rotate(qk_norm(kf, k_gain, eps), cos[:, None, :], sin[:, None, :])
+    cos = np.stack([rope_row(theta, int(p), R)[0] for p in positions]) if n else np.zeros((0, R // 2), np.float32)
+    sin = np.stack([rope_row(theta, int(p), R)[1] for p in positions]) if n else np.zeros((0, R // 2), np.float32)
+    norm = qk_norm_whole if norm_whole else qk_norm
+    qn = rope_rotate(norm(qf, q_gain, eps), cos[:, None, :], sin[:, None, :], R)
+    kn = rope_rotate(norm(kf, k_gain, eps), cos[:, None, :], sin[:, None, :], R)
     q_out = store(qn.reshape(n, n_q_heads * D), pool_dtype)
     k_rows = store(kn, pool_dtype)
     v_rows = store(vf, pool_dtype)
@@ -315,6 +358,14 @@ def prefill(q_out, q_dtype, k_pool, v_pool, pool_dtype, table, rows, positions, 
     """Paged prefill (nest attention.linnet, prefill_paged): token p reads table[rows[p]]."""
     return attention(q_out, q_dtype, k_pool, v_pool, pool_dtype, table, rows,
                      positions, scale, **kw)
+
+
+def output_gate(out, gate, gate_dtype: str) -> np.ndarray:
+    """The sigmoid output gate, float64: fantasma fullAttentionForward multiplies
+    every element of the attention output by ``sigmoid(gate)`` (the gate half of
+    the q projection, same [n, heads*head_dim] layout)."""
+    g = widen(gate, gate_dtype)
+    return np.asarray(out, dtype=np.float64) * (1.0 / (1.0 + np.exp(-g)))
 
 
 def packed(q_out, q_dtype: str, k_rows, v_rows, kv_dtype: str, segments, positions,

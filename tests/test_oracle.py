@@ -380,6 +380,80 @@ def test_segment_mask_equals_paged_rows():
     np.testing.assert_allclose(paged, ref, rtol=1e-12, atol=1e-12)
 
 
+def test_qk_norm_whole_matches_torch_rms_norm_over_all_heads():
+    rng = _rng(20)
+    x = rng.standard_normal((5, 32, 128)).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, 32 * 128).astype(np.float32)
+    got = O.qk_norm_whole(x, g, 1e-6)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x.reshape(5, -1)).double(), (4096,),
+                                       weight=torch.from_numpy(g).double(), eps=1e-6)
+    np.testing.assert_allclose(got.reshape(5, -1), ref.numpy(), rtol=2e-6, atol=1e-6)
+
+
+def test_qk_norm_whole_single_head_is_the_per_head_recipe_bitwise():
+    rng = _rng(21)
+    x = rng.standard_normal((7, 1, 128)).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, 128).astype(np.float32)
+    assert np.array_equal(O.qk_norm_whole(x, g), O.qk_norm(x, g))
+
+
+def test_qk_norm_whole_unit_gain_invariant():
+    # with g = 1: mean of y^2 over all heads = ms / (ms + eps)
+    rng = _rng(22)
+    x = (0.01 * rng.standard_normal((3, 8, 128))).astype(np.float32)
+    y = O.qk_norm_whole(x, np.ones(8 * 128, np.float32)).astype(np.float64)
+    ms = (x.astype(np.float64) ** 2).reshape(3, -1).mean(axis=1)
+    np.testing.assert_allclose((y ** 2).reshape(3, -1).mean(axis=1), ms / (ms + 1e-6), rtol=1e-5)
+
+
+def test_partial_rotary_leaves_the_tail_and_rotates_the_head_bitwise():
+    # fantasma applyRope with rotary_dim R: the first R elements rotate as an
+    # R-wide head would, the others are unchanged
+    rng = _rng(23)
+    y = rng.standard_normal((6, 128)).astype(np.float32)
+    for R in (32, 64, 96):
+        c, s = O.rope_table(O.ROPE_THETA, 6, R)
+        got = O.rope_rotate(y, c, s, R)
+        assert np.array_equal(got[:, R:], y[:, R:])
+        assert np.array_equal(got[:, :R], O.rope_rotate(y[:, :R], c, s))
+    c, s = O.rope_table(O.ROPE_THETA, 6, 128)
+    assert np.array_equal(O.rope_rotate(y, c, s, 128), O.rope_rotate(y, c, s))
+
+
+def test_partial_rotary_scores_depend_on_relative_position_of_rotated_part():
+    # <R(m)q, R(n)k> over the rotated part depends on m - n only; the tail adds a
+    # position-free term
+    rng = _rng(24)
+    R = 32
+    q = rng.standard_normal(128)
+    k = rng.standard_normal(128)
+
+    def rot(x, pos):
+        inv = np.array(O.rope_inv_freq(O.ROPE_THETA, R))
+        a = pos * inv
+        c, s = np.cos(a), np.sin(a)
+        h = R // 2
+        out = x.copy()
+        out[:h] = x[:h] * c - x[h:R] * s
+        out[h:R] = x[h:R] * c + x[:h] * s
+        return out
+
+    d1 = rot(q, 100) @ rot(k, 40)
+    d2 = rot(q, 1060) @ rot(k, 1000)
+    assert abs(d1 - d2) < 1e-9
+    assert abs((rot(q, 5)[R:] @ rot(k, 900)[R:]) - (q[R:] @ k[R:])) == 0.0
+
+
+def test_output_gate_closed_forms():
+    rng = _rng(25)
+    out = rng.standard_normal((3, 256))
+    zero = np.zeros((3, 256), np.float32)
+    assert np.array_equal(O.output_gate(out, zero, "f32"), out * 0.5)
+    g = rng.standard_normal((3, 256)).astype(np.float32)
+    ref = torch.sigmoid(torch.from_numpy(g).double()).numpy() * out
+    np.testing.assert_allclose(O.output_gate(out, g, "f32"), ref, rtol=1e-14, atol=1e-15)
+
+
 def _packed_case(rng, lens, firsts, seg_ids, dtype="f32"):
     seg = np.concatenate([np.full(n, s) for s, n in zip(seg_ids, lens)])
     pos = np.concatenate([np.arange(f, f + n) for f, n in zip(firsts, lens)])
