@@ -120,6 +120,52 @@ int qknorm_rope_append(void* stream, const qkr_pool* pool, int32_t n_tokens,
                        const int32_t* table, int32_t pages_per_row,
                        void* q_out, void* k_pool, void* v_pool);
 
+/* Options of qknorm_rope_append_ex. A null pointer, or all fields 0, gives
+ * qknorm_rope_append. */
+typedef struct qkr_append_opts {
+  int32_t qk_norm_whole;  /* 1: one RMS norm over all heads of q and one over all
+                             heads of k (logicaffeine author.rs, qk_norm_segments
+                             with qk_norm_whole); q_gain then has
+                             num_q_heads*head_dim entries and k_gain
+                             num_kv_heads*head_dim (head h at h*head_dim..).
+                             num_q_heads + num_kv_heads <= 256 (else
+                             QKR_EUNSUPPORTED). 0: per head (default).          */
+  int32_t rotary_dim;     /* R: only elements 0..R-1 of each head rotate, pairs
+                             (i, i + R/2), with rope_cos/rope_sin of width R/2
+                             (qkr_rope_table with head_dim = R); elements R.. pass
+                             unchanged (model.zig applyRope, rotary_dim). Even,
+                             2..head_dim; 0 means head_dim (default).           */
+  int32_t reserved[6];    /* must be 0                                          */
+} qkr_append_opts;
+
+/*
+ * qknorm_rope_append_ex -- qknorm_rope_append with the options above (the
+ * attention variants of the pages: whole-vector QK-norm, partial rotary). The
+ * float32 order of the whole-vector norm: each head's sum of squares as in the
+ * per-head norm, then the head sums added pairwise (neighbours first, an odd last
+ * one carried up), ms = total / (heads*head_dim), r = 1/sqrt(ms + eps).
+ * Invalid options return QKR_EINVAL before anything is enqueued.
+ */
+int qknorm_rope_append_ex(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                          const void* q, const void* k, const void* v, int32_t in_dtype,
+                          const float* q_gain, const float* k_gain, float eps,
+                          const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                          const int32_t* positions,
+                          const int32_t* slots, int32_t n_slotted,
+                          const int32_t* table, int32_t pages_per_row,
+                          void* q_out, void* k_pool, void* v_pool,
+                          const qkr_append_opts* opts);
+
+/* Options of the *_ex attention calls. A null pointer, or all fields 0, gives the
+ * plain call. */
+typedef struct qkr_attn_opts {
+  const void* gate;       /* optional, device, pool dtype, [n][num_q_heads*head_dim]
+                             in the layout of out: every output element is
+                             multiplied by sigmoid(gate) (model.zig,
+                             fullAttentionForward, output gate). null: no gate. */
+  int32_t reserved[6];    /* must be 0                                          */
+} qkr_attn_opts;
+
 /*
  * paged_decode_attn -- one query token per row over that row's pages
  * (attention.linnet, decode_paged / paged_attention).
@@ -147,6 +193,13 @@ int paged_decode_attn(void* stream, const qkr_pool* pool, int32_t n_rows,
 
 size_t paged_decode_attn_workspace(const qkr_pool* pool, int32_t n_rows, int32_t pages_per_row);
 
+/* paged_decode_attn with qkr_attn_opts (output gate). */
+int paged_decode_attn_ex(void* stream, const qkr_pool* pool, int32_t n_rows,
+                         const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* table, int32_t pages_per_row,
+                         const int32_t* positions, float scale, float* out,
+                         void* workspace, size_t workspace_bytes, const qkr_attn_opts* opts);
+
 /*
  * paged_prefill_attn -- packed prompt tokens over their rows' pages
  * (attention.linnet, prefill_paged / paged_prefill_attention).
@@ -173,6 +226,14 @@ int paged_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
 
 size_t paged_prefill_attn_workspace(const qkr_pool* pool, int32_t n_tokens);
 
+/* paged_prefill_attn with qkr_attn_opts (output gate). */
+int paged_prefill_attn_ex(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                          const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
+                          const int32_t* rows, const int32_t* positions,
+                          float scale, float* out, void* workspace, size_t workspace_bytes,
+                          const qkr_attn_opts* opts);
+
 /*
  * packed_prefill_attn -- prompts packed end to end that attend only among
  * themselves (attention.linnet, prefill_packed; on a scratch pool also the
@@ -197,6 +258,14 @@ int packed_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
                         float scale, float* out, void* workspace, size_t workspace_bytes);
 
 size_t packed_prefill_attn_workspace(const qkr_pool* pool, int32_t n_tokens);
+
+/* packed_prefill_attn with qkr_attn_opts (output gate). */
+int packed_prefill_attn_ex(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                           const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
+                           const int32_t* rows, const int32_t* positions, const int32_t* segments,
+                           float scale, float* out, void* workspace, size_t workspace_bytes,
+                           const qkr_attn_opts* opts);
 
 /*
  * qkr_rope_table -- host helper: the RoPE cos/sin table (host memory).

@@ -20,11 +20,15 @@ PAGE_SIZE = 64
 
 EXPORTED = (
     "qknorm_rope_append",
+    "qknorm_rope_append_ex",
     "paged_decode_attn",
+    "paged_decode_attn_ex",
     "paged_decode_attn_workspace",
     "paged_prefill_attn",
+    "paged_prefill_attn_ex",
     "paged_prefill_attn_workspace",
     "packed_prefill_attn",
+    "packed_prefill_attn_ex",
     "packed_prefill_attn_workspace",
     "qkr_rope_table",
     "qkr_status_str",
@@ -42,6 +46,21 @@ class Pool(ctypes.Structure):
         ("num_pages", ctypes.c_int64),
         ("dtype", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
+    ]
+
+
+class AppendOpts(ctypes.Structure):
+    _fields_ = [
+        ("qk_norm_whole", ctypes.c_int32),
+        ("rotary_dim", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 6),
+    ]
+
+
+class AttnOpts(ctypes.Structure):
+    _fields_ = [
+        ("gate", ctypes.c_void_p),
+        ("reserved", ctypes.c_int32 * 6),
     ]
 
 
@@ -63,6 +82,19 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     pool_p = ctypes.POINTER(Pool)
+    app_p = ctypes.POINTER(AppendOpts)
+    att_p = ctypes.POINTER(AttnOpts)
+    lib.qknorm_rope_append_ex.restype = ctypes.c_int
+    lib.qknorm_rope_append_ex.argtypes = [vp, pool_p, i32, vp, vp, vp, i32, vp, vp, f32, vp, vp, i32,
+                                          vp, vp, i32, vp, i32, vp, vp, vp, app_p]
+    lib.paged_decode_attn_ex.restype = ctypes.c_int
+    lib.paged_decode_attn_ex.argtypes = [vp, pool_p, i32, vp, vp, vp, vp, i32, vp, f32, vp, vp, sz, att_p]
+    lib.paged_prefill_attn_ex.restype = ctypes.c_int
+    lib.paged_prefill_attn_ex.argtypes = [vp, pool_p, i32, vp, vp, vp, vp, i32, i32, vp, vp, f32, vp, vp, sz,
+                                          att_p]
+    lib.packed_prefill_attn_ex.restype = ctypes.c_int
+    lib.packed_prefill_attn_ex.argtypes = [vp, pool_p, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, f32, vp, vp,
+                                           sz, att_p]
     lib.qknorm_rope_append.restype = ctypes.c_int
     lib.qknorm_rope_append.argtypes = [vp, pool_p, i32, vp, vp, vp, i32, vp, vp, f32, vp, vp, i32,
                                        vp, vp, i32, vp, i32, vp, vp, vp]
@@ -155,11 +187,14 @@ def rope_table(theta: float, rope_rows: int, head_dim: int = HEAD_DIM):
 
 
 def qknorm_rope_append(q, k, v, q_gain, k_gain, rope_cos, rope_sin, positions, q_out, k_pool,
-                       v_pool, slots=None, table=None, eps: float = 1e-6, stream=None) -> None:
+                       v_pool, slots=None, table=None, eps: float = 1e-6, stream=None,
+                       qk_norm_whole: bool = False, rotary_dim: int = 0) -> None:
     """QK-norm + RoPE of every token of q/k; q_out <- rotated q; k/v written into the pools.
 
     The first ``len(slots)`` tokens write at ``slots``; the rest are decode rows
     whose slot comes from ``table`` (row b = token index - len(slots)).
+    ``qk_norm_whole`` / ``rotary_dim`` select qknorm_rope_append_ex's variants
+    (gains of width heads*head_dim; rope tables of width rotary_dim/2).
     """
     import torch
     n = int(positions.numel())
@@ -168,16 +203,21 @@ def qknorm_rope_append(q, k, v, q_gain, k_gain, rope_cos, rope_sin, positions, q
     n_slotted = 0 if slots is None else int(slots.numel())
     ppr = 0 if table is None else int(table.shape[-1])
     in_dt = _dtype_code(q)
-    st = LIB.qknorm_rope_append(
+    gq = HEAD_DIM * (n_q if qk_norm_whole else 1)
+    gk = HEAD_DIM * (pool.num_kv_heads if qk_norm_whole else 1)
+    rd = int(rotary_dim) or HEAD_DIM
+    opts = AppendOpts(1 if qk_norm_whole else 0, int(rotary_dim))
+    st = LIB.qknorm_rope_append_ex(
         _stream(stream), ctypes.byref(pool), n,
         _ptr(q, "q", q.dtype, n * n_q * HEAD_DIM), _ptr(k, "k", q.dtype, n * pool.num_kv_heads * HEAD_DIM),
         _ptr(v, "v", q.dtype, n * pool.num_kv_heads * HEAD_DIM), in_dt,
-        _ptr(q_gain, "q_gain", torch.float32, HEAD_DIM), _ptr(k_gain, "k_gain", torch.float32, HEAD_DIM),
+        _ptr(q_gain, "q_gain", torch.float32, gq), _ptr(k_gain, "k_gain", torch.float32, gk),
         float(eps), _ptr(rope_cos, "rope_cos", torch.float32), _ptr(rope_sin, "rope_sin", torch.float32),
-        int(rope_cos.shape[0]), _ptr(positions, "positions", torch.int32),
+        int(rope_cos.numel() // (rd // 2)), _ptr(positions, "positions", torch.int32),
         _ptr(slots, "slots", torch.int32), n_slotted,
         _ptr(table, "table", torch.int32, (n - n_slotted) * ppr), ppr,
-        _ptr(q_out, "q_out", k_pool.dtype, n * n_q * HEAD_DIM), _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype))
+        _ptr(q_out, "q_out", k_pool.dtype, n * n_q * HEAD_DIM), _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
+        ctypes.byref(opts))
     _check(st, "qknorm_rope_append")
 
 
@@ -191,40 +231,48 @@ def prefill_workspace_bytes(k_pool, num_q_heads: int, n_tokens: int) -> int:
     return int(LIB.paged_prefill_attn_workspace(ctypes.byref(pool), int(n_tokens)))
 
 
+def _attn_opts(gate, dtype, n):
+    return AttnOpts(_ptr(gate, "gate", dtype, n))
+
+
 def paged_decode_attn(q, k_pool, v_pool, table, positions, scale: float, out, workspace=None,
-                      stream=None) -> None:
-    """out[b] <- attention of row b's query over positions 0..positions[b] of table[b]."""
+                      stream=None, gate=None) -> None:
+    """out[b] <- attention of row b's query over positions 0..positions[b] of table[b]
+    (times sigmoid(gate) when a gate is given)."""
     import torch
     n_q = q.shape[-1] // HEAD_DIM
     pool = pool_desc(k_pool, n_q)
     n_rows = int(positions.numel())
     ppr = int(table.shape[-1])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = LIB.paged_decode_attn(
+    opts = _attn_opts(gate, k_pool.dtype, n_rows * n_q * HEAD_DIM)
+    st = LIB.paged_decode_attn_ex(
         _stream(stream), ctypes.byref(pool), n_rows, _ptr(q, "q", k_pool.dtype, n_rows * n_q * HEAD_DIM),
         _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
         _ptr(table, "table", torch.int32, n_rows * ppr), ppr, _ptr(positions, "positions", torch.int32),
         float(scale), _ptr(out, "out", torch.float32, n_rows * n_q * HEAD_DIM),
-        _ptr(workspace, "workspace"), ws_bytes)
+        _ptr(workspace, "workspace"), ws_bytes, ctypes.byref(opts))
     _check(st, "paged_decode_attn")
 
 
 def paged_prefill_attn(q, k_pool, v_pool, table, rows, positions, scale: float, out, workspace=None,
-                       stream=None) -> None:
-    """out[p] <- attention of token p over positions 0..positions[p] of table[rows[p]]."""
+                       stream=None, gate=None) -> None:
+    """out[p] <- attention of token p over positions 0..positions[p] of table[rows[p]]
+    (times sigmoid(gate) when a gate is given)."""
     import torch
     n_q = q.shape[-1] // HEAD_DIM
     pool = pool_desc(k_pool, n_q)
     n = int(positions.numel())
     ppr = int(table.shape[-1])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = LIB.paged_prefill_attn(
+    opts = _attn_opts(gate, k_pool.dtype, n * n_q * HEAD_DIM)
+    st = LIB.paged_prefill_attn_ex(
         _stream(stream), ctypes.byref(pool), n, _ptr(q, "q", k_pool.dtype, n * n_q * HEAD_DIM),
         _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
         _ptr(table, "table", torch.int32), int(table.shape[0]), ppr,
         _ptr(rows, "rows", torch.int32, n), _ptr(positions, "positions", torch.int32, n),
         float(scale), _ptr(out, "out", torch.float32, n * n_q * HEAD_DIM),
-        _ptr(workspace, "workspace"), ws_bytes)
+        _ptr(workspace, "workspace"), ws_bytes, ctypes.byref(opts))
     _check(st, "paged_prefill_attn")
 
 
@@ -234,7 +282,7 @@ def packed_workspace_bytes(k_pool, num_q_heads: int, n_tokens: int) -> int:
 
 
 def packed_prefill_attn(q, k_pool, v_pool, table, rows, positions, segments, scale: float, out,
-                        workspace=None, stream=None) -> None:
+                        workspace=None, stream=None, gate=None) -> None:
     """out[p] <- attention of token p over the tokens of its own prompt (segment) up to its position."""
     import torch
     n_q = q.shape[-1] // HEAD_DIM
@@ -242,14 +290,15 @@ def packed_prefill_attn(q, k_pool, v_pool, table, rows, positions, segments, sca
     n = int(positions.numel())
     ppr = int(table.shape[-1])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = LIB.packed_prefill_attn(
+    opts = _attn_opts(gate, k_pool.dtype, n * n_q * HEAD_DIM)
+    st = LIB.packed_prefill_attn_ex(
         _stream(stream), ctypes.byref(pool), n, _ptr(q, "q", k_pool.dtype, n * n_q * HEAD_DIM),
         _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
         _ptr(table, "table", torch.int32), int(table.shape[0]), ppr,
         _ptr(rows, "rows", torch.int32, n), _ptr(positions, "positions", torch.int32, n),
         _ptr(segments, "segments", torch.int32, n),
         float(scale), _ptr(out, "out", torch.float32, n * n_q * HEAD_DIM),
-        _ptr(workspace, "workspace"), ws_bytes)
+        _ptr(workspace, "workspace"), ws_bytes, ctypes.byref(opts))
     _check(st, "packed_prefill_attn")
 
 

@@ -41,6 +41,16 @@ int launch_status(hipError_t e) {
   return QKR_ELAUNCH;
 }
 
+// Attention options: the optional output gate; reserved fields must be zero.
+int attn_opts(const qkr_attn_opts* opts, const void** gate) {
+  *gate = nullptr;
+  if (!opts) return QKR_OK;
+  for (int i = 0; i < 6; ++i)
+    if (opts->reserved[i] != 0) return QKR_EINVAL;
+  *gate = opts->gate;
+  return QKR_OK;
+}
+
 // Workspace of the packed form: the bfloat16 kernel's tile schedule, then the
 // first visible position of every token.
 size_t packed_workspace(const qkr_pool* pool, int32_t n_tokens) {
@@ -53,7 +63,10 @@ int prefill_common(void* stream, const qkr_pool* pool, int32_t n_tokens,
                    const void* q, const void* k_pool, const void* v_pool,
                    const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
                    const int32_t* rows, const int32_t* positions, const int32_t* segments,
-                   float scale, float* out, void* workspace, size_t workspace_bytes) {
+                   float scale, float* out, void* workspace, size_t workspace_bytes,
+                   const qkr_attn_opts* opts) {
+  const void* gate = nullptr;
+  if (int os = attn_opts(opts, &gate)) return os;
   int st = check_pool(pool);
   if (st != QKR_OK) return st;
   if (n_tokens < 0) return QKR_EINVAL;
@@ -73,6 +86,7 @@ int prefill_common(void* stream, const qkr_pool* pool, int32_t n_tokens,
   a.rows = rows; a.positions = positions; a.segments = segments;
   a.scale = scale; a.out = out;
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.gate = gate;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t need = segments ? packed_workspace(pool, n_tokens)
                                : (a.bf16 ? qknr::prefill_workspace_bytes(n_tokens, pool->num_kv_heads) : 0);
@@ -119,17 +133,30 @@ int qkr_rope_table(double theta, int32_t rope_rows, int32_t head_dim, float* cos
   return QKR_OK;
 }
 
-int qknorm_rope_append(void* stream, const qkr_pool* pool, int32_t n_tokens,
-                       const void* q, const void* k, const void* v, int32_t in_dtype,
-                       const float* q_gain, const float* k_gain, float eps,
-                       const float* rope_cos, const float* rope_sin, int32_t rope_rows,
-                       const int32_t* positions, const int32_t* slots, int32_t n_slotted,
-                       const int32_t* table, int32_t pages_per_row,
-                       void* q_out, void* k_pool, void* v_pool) {
+int qknorm_rope_append_ex(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                          const void* q, const void* k, const void* v, int32_t in_dtype,
+                          const float* q_gain, const float* k_gain, float eps,
+                          const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                          const int32_t* positions, const int32_t* slots, int32_t n_slotted,
+                          const int32_t* table, int32_t pages_per_row,
+                          void* q_out, void* k_pool, void* v_pool, const qkr_append_opts* opts) {
   int st = check_pool(pool);
   if (st != QKR_OK) return st;
   if (n_tokens < 0 || n_slotted < 0 || n_slotted > n_tokens) return QKR_EINVAL;
   if (in_dtype != QKR_F32 && in_dtype != QKR_BF16) return QKR_EUNSUPPORTED;
+  bool whole = false;
+  int rotary_dim = kHeadDimC;
+  if (opts) {
+    for (int i = 0; i < 6; ++i)
+      if (opts->reserved[i] != 0) return QKR_EINVAL;
+    if (opts->qk_norm_whole != 0 && opts->qk_norm_whole != 1) return QKR_EINVAL;
+    whole = opts->qk_norm_whole == 1;
+    if (opts->rotary_dim != 0) {
+      if (opts->rotary_dim < 2 || opts->rotary_dim > kHeadDimC || opts->rotary_dim % 2 != 0) return QKR_EINVAL;
+      rotary_dim = opts->rotary_dim;
+    }
+    if (whole && pool->num_q_heads + pool->num_kv_heads > qknr::append_max_whole_heads()) return QKR_EUNSUPPORTED;
+  }
   if (n_tokens == 0) return QKR_OK;
   if (!q || !k || !v || !q_gain || !k_gain || !rope_cos || !rope_sin || !positions || !q_out ||
       !k_pool || !v_pool)
@@ -150,7 +177,21 @@ int qknorm_rope_append(void* stream, const qkr_pool* pool, int32_t n_tokens,
   a.positions = positions; a.slots = slots; a.n_slotted = n_slotted;
   a.table = table; a.pages_per_row = pages_per_row; a.num_pages = pool->num_pages;
   a.q_out = q_out; a.k_pool = k_pool; a.v_pool = v_pool;
+  a.norm_whole = whole;
+  a.rotary_dim = rotary_dim;
   return launch_status(qknr::launch_append(static_cast<hipStream_t>(stream), a));
+}
+
+int qknorm_rope_append(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                       const void* q, const void* k, const void* v, int32_t in_dtype,
+                       const float* q_gain, const float* k_gain, float eps,
+                       const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                       const int32_t* positions, const int32_t* slots, int32_t n_slotted,
+                       const int32_t* table, int32_t pages_per_row,
+                       void* q_out, void* k_pool, void* v_pool) {
+  return qknorm_rope_append_ex(stream, pool, n_tokens, q, k, v, in_dtype, q_gain, k_gain, eps,
+                               rope_cos, rope_sin, rope_rows, positions, slots, n_slotted, table,
+                               pages_per_row, q_out, k_pool, v_pool, nullptr);
 }
 
 size_t paged_decode_attn_workspace(const qkr_pool* pool, int32_t n_rows, int32_t pages_per_row) {
@@ -159,11 +200,13 @@ size_t paged_decode_attn_workspace(const qkr_pool* pool, int32_t n_rows, int32_t
   return qknr::decode_workspace_bytes(n_rows, pool->num_kv_heads, pages_per_row);
 }
 
-int paged_decode_attn(void* stream, const qkr_pool* pool, int32_t n_rows,
-                      const void* q, const void* k_pool, const void* v_pool,
-                      const int32_t* table, int32_t pages_per_row,
-                      const int32_t* positions, float scale, float* out,
-                      void* workspace, size_t workspace_bytes) {
+int paged_decode_attn_ex(void* stream, const qkr_pool* pool, int32_t n_rows,
+                         const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* table, int32_t pages_per_row,
+                         const int32_t* positions, float scale, float* out,
+                         void* workspace, size_t workspace_bytes, const qkr_attn_opts* opts) {
+  const void* gate = nullptr;
+  if (int os = attn_opts(opts, &gate)) return os;
   int st = check_pool(pool);
   if (st != QKR_OK) return st;
   if (n_rows < 0) return QKR_EINVAL;
@@ -180,6 +223,7 @@ int paged_decode_attn(void* stream, const qkr_pool* pool, int32_t n_rows,
   a.table = table; a.n_table_rows = n_rows; a.pages_per_row = pages_per_row;
   a.rows = nullptr; a.positions = positions; a.scale = scale; a.out = out;
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.gate = gate;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!a.bf16) return launch_status(qknr::launch_attention_generic(s, a));
   if (n_rows > qknr::decode_max_rows()) return QKR_EUNSUPPORTED;
@@ -188,10 +232,30 @@ int paged_decode_attn(void* stream, const qkr_pool* pool, int32_t n_rows,
   return launch_status(qknr::launch_decode_bf16(s, a));
 }
 
+int paged_decode_attn(void* stream, const qkr_pool* pool, int32_t n_rows,
+                      const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* table, int32_t pages_per_row,
+                      const int32_t* positions, float scale, float* out,
+                      void* workspace, size_t workspace_bytes) {
+  return paged_decode_attn_ex(stream, pool, n_rows, q, k_pool, v_pool, table, pages_per_row,
+                              positions, scale, out, workspace, workspace_bytes, nullptr);
+}
+
 size_t paged_prefill_attn_workspace(const qkr_pool* pool, int32_t n_tokens) {
   if (check_pool(pool) != QKR_OK || n_tokens <= 0) return 0;
   if (pool->dtype != QKR_BF16) return 0;
   return qknr::prefill_workspace_bytes(n_tokens, pool->num_kv_heads);
+}
+
+int paged_prefill_attn_ex(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                          const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
+                          const int32_t* rows, const int32_t* positions,
+                          float scale, float* out, void* workspace, size_t workspace_bytes,
+                          const qkr_attn_opts* opts) {
+  return prefill_common(stream, pool, n_tokens, q, k_pool, v_pool, table, n_table_rows,
+                        pages_per_row, rows, positions, nullptr, scale, out, workspace,
+                        workspace_bytes, opts);
 }
 
 int paged_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
@@ -199,9 +263,9 @@ int paged_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
                        const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
                        const int32_t* rows, const int32_t* positions,
                        float scale, float* out, void* workspace, size_t workspace_bytes) {
-  return prefill_common(stream, pool, n_tokens, q, k_pool, v_pool, table, n_table_rows,
-                        pages_per_row, rows, positions, nullptr, scale, out, workspace,
-                        workspace_bytes);
+  return paged_prefill_attn_ex(stream, pool, n_tokens, q, k_pool, v_pool, table, n_table_rows,
+                               pages_per_row, rows, positions, scale, out, workspace,
+                               workspace_bytes, nullptr);
 }
 
 size_t packed_prefill_attn_workspace(const qkr_pool* pool, int32_t n_tokens) {
@@ -209,15 +273,26 @@ size_t packed_prefill_attn_workspace(const qkr_pool* pool, int32_t n_tokens) {
   return packed_workspace(pool, n_tokens);
 }
 
+int packed_prefill_attn_ex(void* stream, const qkr_pool* pool, int32_t n_tokens,
+                           const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
+                           const int32_t* rows, const int32_t* positions, const int32_t* segments,
+                           float scale, float* out, void* workspace, size_t workspace_bytes,
+                           const qkr_attn_opts* opts) {
+  if (!segments && n_tokens > 0) return QKR_EINVAL;
+  return prefill_common(stream, pool, n_tokens, q, k_pool, v_pool, table, n_table_rows,
+                        pages_per_row, rows, positions, segments, scale, out, workspace,
+                        workspace_bytes, opts);
+}
+
 int packed_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
                         const void* q, const void* k_pool, const void* v_pool,
                         const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
                         const int32_t* rows, const int32_t* positions, const int32_t* segments,
                         float scale, float* out, void* workspace, size_t workspace_bytes) {
-  if (!segments && n_tokens > 0) return QKR_EINVAL;
-  return prefill_common(stream, pool, n_tokens, q, k_pool, v_pool, table, n_table_rows,
-                        pages_per_row, rows, positions, segments, scale, out, workspace,
-                        workspace_bytes);
+  return packed_prefill_attn_ex(stream, pool, n_tokens, q, k_pool, v_pool, table, n_table_rows,
+                                pages_per_row, rows, positions, segments, scale, out, workspace,
+                                workspace_bytes, nullptr);
 }
 
 }  // extern "C"

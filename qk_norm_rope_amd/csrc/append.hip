@@ -48,15 +48,35 @@ template <> struct Vec4<uint16_t> {
   }
 };
 
-template <typename TIn, typename TOut>
+// Pairwise float32 sum of n values, neighbours first, an odd last one carried up
+// a level (the order the whole-vector norm pins). v (in LDS) is overwritten.
+__device__ __forceinline__ float pair_sums(float* v, int n) {
+  while (n > 1) {
+    const int m = n & ~1;
+    for (int i = 0; i < m; i += 2) v[i >> 1] = v[i] + v[i + 1];
+    if (n & 1) v[m >> 1] = v[m];
+    n = (n + 1) >> 1;
+  }
+  return v[0];
+}
+
+constexpr int kMaxWholeHeads = 256;   // q heads + kv heads for the whole-vector norm
+
+// WHOLE: one RMS norm over all heads of q and over all heads of k (gains of width
+// heads*head_dim). PARTIAL: only the first rotary_dim elements of a head rotate.
+template <typename TIn, typename TOut, bool WHOLE, bool PARTIAL>
 __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(
     int n_q_heads, int n_kv_heads,
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ q_gain, const float* __restrict__ k_gain, float eps,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rope_rows,
+    int rotary_dim,
     const int* __restrict__ positions, const int* __restrict__ slots, int n_slotted,
     const int* __restrict__ table, int pages_per_row, int64_t num_pages,
     TOut* __restrict__ q_out, TOut* __restrict__ k_pool, TOut* __restrict__ v_pool) {
+  __shared__ float s_ss[WHOLE ? 2 : 1][WHOLE ? kMaxWholeHeads : 1];
+  __shared__ float s_r[2];
+  __shared__ float s_y[PARTIAL ? 16 : 1][PARTIAL ? kHeadDim : 1];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int pos = positions[t];
@@ -77,33 +97,23 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(
   if (slot >= pool_slots) slot = -1;
 
   const int j = tid & 15;
-  const float* cs = rope_cos + (int64_t)pos * (kHeadDim / 2) + 4 * j;
-  const float* sn = rope_sin + (int64_t)pos * (kHeadDim / 2) + 4 * j;
+  const int grp = tid >> 4;
+  const int half_r = PARTIAL ? rotary_dim / 2 : kHeadDim / 2;
   float c[4], s[4];
-  Vec4<float>::load(cs, c);
-  Vec4<float>::load(sn, s);
+  if (!PARTIAL) {
+    Vec4<float>::load(rope_cos + (int64_t)pos * (kHeadDim / 2) + 4 * j, c);
+    Vec4<float>::load(rope_sin + (int64_t)pos * (kHeadDim / 2) + 4 * j, s);
+  }
+  const float* cs_row = rope_cos + (int64_t)pos * half_r;
+  const float* sn_row = rope_sin + (int64_t)pos * half_r;
 
   const int n_norm = n_q_heads + n_kv_heads;
-  for (int hv = tid >> 4; hv < n_norm; hv += 16) {
-    const TIn* src;
-    const float* g;
-    TOut* dst;
-    bool write = true;
-    if (hv < n_q_heads) {
-      src = q + ((int64_t)t * n_q_heads + hv) * kHeadDim;
-      g = q_gain;
-      dst = q_out + ((int64_t)t * n_q_heads + hv) * kHeadDim;
-    } else {
-      const int kh = hv - n_q_heads;
-      src = k + ((int64_t)t * n_kv_heads + kh) * kHeadDim;
-      g = k_gain;
-      write = slot >= 0;
-      dst = k_pool + ((int64_t)kh * pool_slots + (write ? slot : 0)) * kHeadDim;
-    }
-    float a[4], b[4];
-    Vec4<TIn>::load(src + 4 * j, a);
-    Vec4<TIn>::load(src + kHeadDim / 2 + 4 * j, b);
-
+  auto source = [&](int hv) -> const TIn* {
+    return hv < n_q_heads ? q + ((int64_t)t * n_q_heads + hv) * kHeadDim
+                          : k + ((int64_t)t * n_kv_heads + (hv - n_q_heads)) * kHeadDim;
+  };
+  // per-head sum of squares: lane j holds elements 4j..4j+3 of each half
+  auto head_ss = [&](const float (&a)[4], const float (&b)[4]) {
     float p0 = a[0] * a[0] + b[0] * b[0];
     float p1 = a[1] * a[1] + b[1] * b[1];
     float p2 = a[2] * a[2] + b[2] * b[2];
@@ -113,23 +123,109 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(
     ss = ss + __shfl_xor(ss, 2, 16);
     ss = ss + __shfl_xor(ss, 4, 16);
     ss = ss + __shfl_xor(ss, 8, 16);
-    const float ms = ss * (1.0f / kHeadDim);
-    const float r = 1.0f / __builtin_sqrtf(ms + eps);
+    return ss;
+  };
+
+  if (WHOLE) {
+    for (int hv = grp; hv < n_norm; hv += 16) {
+      float a[4], b[4];
+      Vec4<TIn>::load(source(hv) + 4 * j, a);
+      Vec4<TIn>::load(source(hv) + kHeadDim / 2 + 4 * j, b);
+      const float ss = head_ss(a, b);
+      if (j == 0) {
+        if (hv < n_q_heads) s_ss[0][hv] = ss;
+        else s_ss[1][hv - n_q_heads] = ss;
+      }
+    }
+    __syncthreads();
+    if (tid < 2) {   // thread 0: the q heads' sums, thread 1: the k heads'
+      const int nh = tid == 0 ? n_q_heads : n_kv_heads;
+      const float total = pair_sums(s_ss[tid], nh);
+      const float ms = total / (float)(nh * kHeadDim);
+      s_r[tid] = 1.0f / __builtin_sqrtf(ms + eps);
+    }
+    __syncthreads();
+  }
+
+  for (int hv = grp; hv < n_norm; hv += 16) {
+    const TIn* src = source(hv);
+    const float* g;
+    TOut* dst;
+    bool write = true;
+    int hl;   // head index within q or k
+    if (hv < n_q_heads) {
+      hl = hv;
+      g = q_gain;
+      dst = q_out + ((int64_t)t * n_q_heads + hv) * kHeadDim;
+    } else {
+      hl = hv - n_q_heads;
+      g = k_gain;
+      write = slot >= 0;
+      dst = k_pool + ((int64_t)hl * pool_slots + (write ? slot : 0)) * kHeadDim;
+    }
+    if (WHOLE) g += (int64_t)hl * kHeadDim;
+    float a[4], b[4];
+    Vec4<TIn>::load(src + 4 * j, a);
+    Vec4<TIn>::load(src + kHeadDim / 2 + 4 * j, b);
+
+    float r;
+    if (WHOLE) {
+      r = s_r[hv < n_q_heads ? 0 : 1];
+    } else {
+      const float ms = head_ss(a, b) * (1.0f / kHeadDim);
+      r = 1.0f / __builtin_sqrtf(ms + eps);
+    }
 
     float ga[4], gb[4];
     Vec4<float>::load(g + 4 * j, ga);
     Vec4<float>::load(g + kHeadDim / 2 + 4 * j, gb);
-    float oa[4], ob[4];
+    float ya[4], yb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float ya = (a[i] * r) * ga[i];
-      const float yb = (b[i] * r) * gb[i];
-      const float ac = ya * c[i];
-      const float bs = yb * s[i];
-      const float bc = yb * c[i];
-      const float as = ya * s[i];
-      oa[i] = ac - bs;
-      ob[i] = bc + as;
+      ya[i] = (a[i] * r) * ga[i];
+      yb[i] = (b[i] * r) * gb[i];
+    }
+    float oa[4], ob[4];
+    if (!PARTIAL) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ac = ya[i] * c[i];
+        const float bs = yb[i] * s[i];
+        const float bc = yb[i] * c[i];
+        const float as = ya[i] * s[i];
+        oa[i] = ac - bs;
+        ob[i] = bc + as;
+      }
+    } else {
+      // pairs (e, e + R/2) for e < R/2 may sit in other lanes of the 16: go through LDS
+      // (the 16 lanes of a head are one wave, so program order orders the accesses)
+      float* yrow = s_y[grp];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        yrow[4 * j + i] = ya[i];
+        yrow[kHeadDim / 2 + 4 * j + i] = yb[i];
+      }
+      __builtin_amdgcn_wave_barrier();
+      auto rot = [&](int e, float y) -> float {
+        if (e < half_r) {
+          const float ye = y * cs_row[e];
+          const float ps = yrow[e + half_r] * sn_row[e];
+          return ye - ps;
+        }
+        if (e < rotary_dim) {
+          const int i = e - half_r;
+          const float ye = y * cs_row[i];
+          const float ps = yrow[i] * sn_row[i];
+          return ye + ps;
+        }
+        return y;
+      };
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        oa[i] = rot(4 * j + i, ya[i]);
+        ob[i] = rot(kHeadDim / 2 + 4 * j + i, yb[i]);
+      }
+      __builtin_amdgcn_wave_barrier();   // the row is rewritten by the group's next head
     }
     if (write) {
       Vec4<TOut>::store(dst + 4 * j, oa);
@@ -151,20 +247,32 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(
 
 }  // namespace
 
-hipError_t launch_append(hipStream_t stream, const AppendArgs& a) {
+template <typename TI, typename TO>
+static void launch_typed(hipStream_t stream, const AppendArgs& a) {
   const dim3 grid(a.n_tokens), block(256);
-#define QKNR_APPEND(TI, TO)                                                            \
-  hipLaunchKernelGGL((qknorm_rope_append_kernel<TI, TO>), grid, block, 0, stream,       \
-                     a.n_q_heads, a.n_kv_heads, (const TI*)a.q, (const TI*)a.k,         \
-                     (const TI*)a.v, a.q_gain, a.k_gain, a.eps, a.rope_cos, a.rope_sin, \
-                     a.rope_rows, a.positions, a.slots, a.n_slotted, a.table,           \
-                     a.pages_per_row, a.num_pages, (TO*)a.q_out, (TO*)a.k_pool,         \
-                     (TO*)a.v_pool)
-  if (a.in_bf16 && a.out_bf16) QKNR_APPEND(uint16_t, uint16_t);
-  else if (a.in_bf16) QKNR_APPEND(uint16_t, float);
-  else if (a.out_bf16) QKNR_APPEND(float, uint16_t);
-  else QKNR_APPEND(float, float);
+  const int rd = a.rotary_dim;
+  const bool partial = rd != kHeadDim;
+#define QKNR_APPEND(W, PT)                                                                 \
+  hipLaunchKernelGGL((qknorm_rope_append_kernel<TI, TO, W, PT>), grid, block, 0, stream,     \
+                     a.n_q_heads, a.n_kv_heads, (const TI*)a.q, (const TI*)a.k,             \
+                     (const TI*)a.v, a.q_gain, a.k_gain, a.eps, a.rope_cos, a.rope_sin,     \
+                     a.rope_rows, rd, a.positions, a.slots, a.n_slotted, a.table,           \
+                     a.pages_per_row, a.num_pages, (TO*)a.q_out, (TO*)a.k_pool, (TO*)a.v_pool)
+  if (a.norm_whole) {
+    if (partial) QKNR_APPEND(true, true); else QKNR_APPEND(true, false);
+  } else {
+    if (partial) QKNR_APPEND(false, true); else QKNR_APPEND(false, false);
+  }
 #undef QKNR_APPEND
+}
+
+int append_max_whole_heads() { return kMaxWholeHeads; }
+
+hipError_t launch_append(hipStream_t stream, const AppendArgs& a) {
+  if (a.in_bf16 && a.out_bf16) launch_typed<uint16_t, uint16_t>(stream, a);
+  else if (a.in_bf16) launch_typed<uint16_t, float>(stream, a);
+  else if (a.out_bf16) launch_typed<float, uint16_t>(stream, a);
+  else launch_typed<float, float>(stream, a);
   return hipGetLastError();
 }
 

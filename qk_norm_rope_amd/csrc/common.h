@@ -41,6 +41,10 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Logistic function 1 / (1 + e^-x): the attention output gate (fantasma
+// "src/inference/model.zig", fullAttentionForward: attn_out *= sigmoid(gate)).
+__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
 // Broadcast lane 0's value to the whole wave (result lives in a scalar register).
 __device__ __forceinline__ float lane0(float x) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));

@@ -54,6 +54,7 @@ struct DecodeParams {
   float* out;
   int* counters;      // [n_rows * n_kv], zero between calls
   float* partials;    // [grid][2][kPartial]
+  const uint16_t* gate;   // optional output gate [n_rows][n_q*128], bf16
 };
 
 // max over the 16 lanes of a DPP row, result in every lane of the row
@@ -317,9 +318,16 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(DecodeParams P) 
       A1 += f * s_acc[ww][hi][dd + 1];
     }
     float* orow = P.out + ((int64_t)b * n_q + g * kGroup + hi) * kHeadDim + dd;
+    // output gate: out *= sigmoid(gate) at the same element
+    float g0 = 1.f, g1 = 1.f;
+    if (P.gate) {
+      const uint32_t gw = *reinterpret_cast<const uint32_t*>(P.gate + ((int64_t)b * n_q + g * kGroup + hi) * kHeadDim + dd);
+      g0 = sigmoidf(bf16_lo(gw));
+      g1 = sigmoidf(bf16_hi(gw));
+    }
     if (whole) {
-      orow[0] = A0 / L;
-      orow[1] = A1 / L;
+      orow[0] = (A0 / L) * g0;
+      orow[1] = (A1 / L) * g1;
     } else {
       const int slot = first_segment ? 0 : 1;
       float* part = P.partials + ((int64_t)gi * 2 + slot) * kPartial + hi * (kHeadDim + 2);
@@ -368,8 +376,8 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(DecodeParams P) 
             Mx = mn;
           }
         }
-        orow[0] = B0 / Lt;
-        orow[1] = B1 / Lt;
+        orow[0] = (B0 / Lt) * g0;
+        orow[1] = (B1 / Lt) * g1;
         if (tid == 0) __hip_atomic_store(&P.counters[rg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -423,6 +431,7 @@ hipError_t launch_decode_bf16(hipStream_t stream, const AttnArgs& a) {
   P.positions = a.positions;
   P.scale_log2 = a.scale * kLog2e;
   P.out = a.out;
+  P.gate = (const uint16_t*)a.gate;
   P.counters = static_cast<int*>(a.workspace);
   P.partials = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + counter_bytes);
   const int grid = grid_for_device();

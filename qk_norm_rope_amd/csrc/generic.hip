@@ -28,7 +28,8 @@ __global__ __launch_bounds__(256) void attention_generic_kernel(
     int n_q_heads, const T* __restrict__ q, const T* __restrict__ k_pool,
     const T* __restrict__ v_pool, int64_t num_pages, const int* __restrict__ table,
     int n_table_rows, int pages_per_row, const int* __restrict__ rows,
-    const int* __restrict__ positions, const int* __restrict__ lo, float scale, float* __restrict__ out) {
+    const int* __restrict__ positions, const int* __restrict__ lo, const T* __restrict__ gate,
+    float scale, float* __restrict__ out) {
   const int t = blockIdx.x;
   const int g = blockIdx.y;
   const int w = threadIdx.x >> 6;
@@ -66,8 +67,14 @@ __global__ __launch_bounds__(256) void attention_generic_kernel(
     a1 = a1 * corr + p * v1;
     m = mn;
   }
-  o[0] = a0 / l;
-  o[1] = a1 / l;
+  float g0 = 1.f, g1 = 1.f;
+  if (gate) {   // output gate: out *= sigmoid(gate) at the same element
+    load2<T>(gate + ((int64_t)t * n_q_heads + h) * kHeadDim + 2 * lane, g0, g1);
+    g0 = sigmoidf(g0);
+    g1 = sigmoidf(g1);
+  }
+  o[0] = (a0 / l) * g0;
+  o[1] = (a1 / l) * g1;
 }
 
 }  // namespace
@@ -84,12 +91,12 @@ hipError_t launch_attention_generic(hipStream_t stream, const AttnArgs& a) {
     hipLaunchKernelGGL(attention_generic_kernel<uint16_t>, grid, block, 0, stream, a.n_q_heads,
                        (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,
                        a.num_pages, a.table, a.n_table_rows, a.pages_per_row, a.rows,
-                       a.positions, lo, a.scale, a.out);
+                       a.positions, lo, (const uint16_t*)a.gate, a.scale, a.out);
   } else {
     hipLaunchKernelGGL(attention_generic_kernel<float>, grid, block, 0, stream, a.n_q_heads,
                        (const float*)a.q, (const float*)a.k_pool, (const float*)a.v_pool,
                        a.num_pages, a.table, a.n_table_rows, a.pages_per_row, a.rows,
-                       a.positions, lo, a.scale, a.out);
+                       a.positions, lo, (const float*)a.gate, a.scale, a.out);
   }
   return hipGetLastError();
 }

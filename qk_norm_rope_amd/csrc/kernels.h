@@ -21,6 +21,8 @@ struct AppendArgs {
   int pages_per_row;
   int64_t num_pages;
   void *q_out, *k_pool, *v_pool;
+  bool norm_whole = false;   // one RMS norm over all heads (gains heads*head_dim wide)
+  int rotary_dim = 128;      // elements of each head that rotate (pairs (i, i + rotary_dim/2))
 };
 
 struct AttnArgs {
@@ -35,6 +37,7 @@ struct AttnArgs {
   const int32_t* rows;    // prefill: row of each token; decode: nullptr (row = index)
   const int32_t* positions;
   const int32_t* segments = nullptr;   // packed prefill: prompt of each token, else nullptr
+  const void* gate = nullptr;          // optional output gate (pool dtype), out *= sigmoid(gate)
   float scale;
   float* out;
   void* workspace;
@@ -42,6 +45,7 @@ struct AttnArgs {
 };
 
 hipError_t launch_append(hipStream_t stream, const AppendArgs& a);
+int append_max_whole_heads();
 
 // Decode: split-K over page ranges with a fused last-arriver merge.
 size_t decode_workspace_bytes(int n_rows, int n_kv_heads, int pages_per_row);

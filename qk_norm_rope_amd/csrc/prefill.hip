@@ -130,6 +130,7 @@ struct PrefillParams {
   float* out;
   const int* order;
   const int* lo;   // first visible position per token (packed form), or null (0)
+  const uint16_t* gate;   // optional output gate [n_tokens][n_q*128], bf16
 };
 
 __device__ __forceinline__ bf16x8 join(i16x4 a, i16x4 b) {
@@ -547,12 +548,20 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
       const int t = t0 + qn;
       const float inv = 1.0f / lt;
       float* op = P.out + ((int64_t)t * n_q + head) * kHeadDim + 4 * lh;
+      const uint16_t* gp = P.gate ? P.gate + ((int64_t)t * n_q + head) * kHeadDim + 4 * lh : nullptr;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4 v4 = {o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv, o[dt][4 * j + 2] * inv,
-                            o[dt][4 * j + 3] * inv};
+          f32x4 v4 = {o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv, o[dt][4 * j + 2] * inv,
+                      o[dt][4 * j + 3] * inv};
+          if (gp) {   // output gate: out *= sigmoid(gate) at the same element
+            const uint2 gw = *reinterpret_cast<const uint2*>(gp + 32 * dt + 8 * j);
+            v4[0] *= sigmoidf(bf16_lo(gw.x));
+            v4[1] *= sigmoidf(bf16_hi(gw.x));
+            v4[2] *= sigmoidf(bf16_lo(gw.y));
+            v4[3] *= sigmoidf(bf16_hi(gw.y));
+          }
           *reinterpret_cast<f32x4*>(op + 32 * dt + 8 * j) = v4;
         }
     }
@@ -609,6 +618,7 @@ hipError_t launch_prefill_bf16(hipStream_t stream, const AttnArgs& a) {
   P.out = a.out;
   P.order = order;
   P.lo = lo;
+  P.gate = (const uint16_t*)a.gate;
   hipLaunchKernelGGL(paged_prefill_bf16_kernel, dim3(n_tiles * a.n_kv_heads), dim3(512), 0, stream, P);
   return hipGetLastError();
 }

@@ -43,6 +43,10 @@ def test_rope_table_matches_oracle_bitwise():
     ocos, osin = O.rope_table(1e6, 40960, 128)
     assert np.array_equal(cos, ocos)
     assert np.array_equal(sin, osin)
+    for r in (2, 32, 64, 96):   # partial rotary: the table of an r-wide head
+        cos, sin = Q.rope_table(1e6, 300, r)
+        ocos, osin = O.rope_table(1e6, 300, r)
+        assert np.array_equal(cos, ocos) and np.array_equal(sin, osin)
 
 
 def _pool(**kw):
@@ -106,6 +110,52 @@ def test_decode_and_prefill_host_checks():
                                   FAKE, 0.1, FAKE, FAKE, pneed - 1) == -3
     assert lib.paged_prefill_attn(None, ctypes.byref(_pool(head_dim=256)), 100, FAKE, FAKE, FAKE,
                                   FAKE, 3, 4, FAKE, FAKE, 0.1, FAKE, FAKE, pneed) == -2
+
+
+def _append_ex(pool, opts, **kw):
+    args = dict(stream=None, n=1, q=FAKE, k=FAKE, v=FAKE, in_dtype=L.QKR_BF16, qg=FAKE, kg=FAKE,
+                eps=1e-6, cos=FAKE, sin=FAKE, rope_rows=100, pos=FAKE, slots=FAKE, n_slotted=1,
+                table=None, ppr=0, q_out=FAKE, kp=FAKE, vp=FAKE)
+    args.update(kw)
+    return L.LIB.qknorm_rope_append_ex(args["stream"], ctypes.byref(pool), args["n"], args["q"], args["k"],
+                                       args["v"], args["in_dtype"], args["qg"], args["kg"], args["eps"],
+                                       args["cos"], args["sin"], args["rope_rows"], args["pos"],
+                                       args["slots"], args["n_slotted"], args["table"], args["ppr"],
+                                       args["q_out"], args["kp"], args["vp"],
+                                       ctypes.byref(opts) if opts is not None else None)
+
+
+def test_append_options_host_checks():
+    n0 = dict(n=0, n_slotted=0)   # valid options on an empty batch: no-op
+    assert _append_ex(_pool(), None, **n0) == 0
+    assert _append_ex(_pool(), L.AppendOpts(1, 64), **n0) == 0
+    assert _append_ex(_pool(), L.AppendOpts(2, 0)) == -1            # qk_norm_whole is 0 or 1
+    for bad in (1, 3, 130, -2):                                      # odd, too wide, negative
+        assert _append_ex(_pool(), L.AppendOpts(0, bad)) == -1
+    o = L.AppendOpts(0, 0)
+    o.reserved[2] = 1
+    assert _append_ex(_pool(), o) == -1
+    assert _append_ex(_pool(num_q_heads=256, num_kv_heads=64), L.AppendOpts(1, 0)) == -2
+
+
+def test_attention_options_host_checks():
+    pool = _pool()
+    lib = L.LIB
+    o = L.AttnOpts(None)
+    o.reserved[0] = 5
+    need = lib.paged_decode_attn_workspace(ctypes.byref(pool), 2, 4)
+    assert lib.paged_decode_attn_ex(None, ctypes.byref(pool), 2, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+                                    0.1, FAKE, FAKE, need, ctypes.byref(o)) == -1
+    assert lib.paged_prefill_attn_ex(None, ctypes.byref(pool), 100, FAKE, FAKE, FAKE, FAKE, 3, 4, FAKE,
+                                     FAKE, 0.1, FAKE, FAKE, 1 << 20, ctypes.byref(o)) == -1
+    assert lib.packed_prefill_attn_ex(None, ctypes.byref(pool), 100, FAKE, FAKE, FAKE, FAKE, 3, 4, FAKE,
+                                      FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 20, ctypes.byref(o)) == -1
+    # the packed form needs segments, and its workspace also holds first positions
+    assert lib.packed_prefill_attn(None, ctypes.byref(pool), 100, FAKE, FAKE, FAKE, FAKE, 3, 4, FAKE,
+                                   FAKE, None, 0.1, FAKE, FAKE, 1 << 20) == -1
+    assert lib.packed_prefill_attn_workspace(ctypes.byref(pool), 100) > \
+        lib.paged_prefill_attn_workspace(ctypes.byref(pool), 100)
+    assert lib.packed_prefill_attn_workspace(ctypes.byref(_pool(dtype=L.QKR_F32)), 100) >= 400
 
 
 def test_workspace_sizes_grow_with_work():
