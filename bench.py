@@ -97,6 +97,49 @@ def measure_packed(Q, W, w, t, q_out, k_pool, v_pool, out, stream, reps=10):
             "form": "each chunk attends only to itself (no history)"}
 
 
+def measure_variants(Q, W, w, t, positions_all, q_out, k_pool, v_pool, dec_out, ws_d, stream, reps=10):
+    """The attention variants on the step's inputs, timed after the step's timed
+    region: the append with one norm over all heads and a 64-wide rotation, and
+    the decode with the sigmoid output gate."""
+    import numpy as np
+    import torch
+    dev = q_out.device
+    work = algorithmic_work(w)
+    rng = np.random.default_rng(7)
+    gq = torch.from_numpy(rng.uniform(0.5, 1.5, 32 * 128).astype(np.float32)).to(dev)
+    gk = torch.from_numpy(rng.uniform(0.5, 1.5, 8 * 128).astype(np.float32)).to(dev)
+    c64, s64 = Q.rope_table(1e6, W.MAX_POSITIONS, 64)
+    c64, s64 = torch.from_numpy(c64).to(dev), torch.from_numpy(s64).to(dev)
+    P, R = w.n_prefill, w.n_decode
+
+    def timed(fn):
+        fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / reps
+
+    app_ms = timed(lambda: Q.qknorm_rope_append(
+        t["q"], t["k"], t["v"], gq, gk, c64, s64, positions_all, q_out, k_pool, v_pool,
+        slots=t["slots"] if P else None, table=t["decode_table"] if R else None,
+        qk_norm_whole=True, rotary_dim=64))
+    # the extra gain bytes of the whole-vector norm are read once per token from cache; not counted
+    out = {"append_whole_norm_rotary64": {"gbs": round(work["append_bytes"] / (app_ms * 1e-3) / 1e9, 2),
+                                          "ms_per_launch": round(app_ms, 5), "bound": "hbm"}}
+    if R:
+        gate = torch.randn((R, 32 * 128), device=dev).to(torch.bfloat16)
+        dec_ms = timed(lambda: Q.paged_decode_attn(q_out[P:], k_pool, v_pool, t["decode_table"],
+                                                   t["step_positions"], W.SCALE, dec_out, ws_d, gate=gate))
+        gbs = (work["decode_bytes"] + R * 32 * 128 * 2) / (dec_ms * 1e-3) / 1e9
+        out["decode_gated"] = {"gbs": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                               "ms_per_launch": round(dec_ms, 5), "bound": "hbm"}
+    return out
+
+
 def oracle_snapshot(w, k_pool, v_pool, sample_rows=128, prefill_tokens=256, seed=0):
     """Host copies of the pool slots the oracle sample reads, taken from the
     generator's pre-step pools before any library kernel has run."""
@@ -286,6 +329,7 @@ def main():
     step_ms = sum(times.values())
 
     packed = measure_packed(Q, W, w, t, q_out, k_pool, v_pool, pre_out, stream) if P else None
+    variants = measure_variants(Q, W, w, t, positions_all, q_out, k_pool, v_pool, dec_out, ws_d, stream)
 
     work = algorithmic_work(w)
     dec_gbs = work["decode_bytes"] / (times["decode"] * 1e-3) / 1e9 if R else 0.0
@@ -324,6 +368,7 @@ def main():
     }
     if packed is not None:
         result["packed_prefill"] = packed
+    result["variants"] = variants
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, snap)
     print(json.dumps(result), flush=True)
