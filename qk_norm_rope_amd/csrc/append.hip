@@ -7,8 +7,8 @@
 // src/norm.linnet, src/rope.linnet. fantasma "src/inference/model.zig":
 // fullAttentionForward and applyRope (rotate_half pairing of i with i + 64).
 //
-// One workgroup per token; 16 lanes per head vector, lane j holding elements
-// 4j..4j+3 of each half. The float32 arithmetic is fixed (no contraction into
+// One workgroup per token; 8 lanes per head vector, lane j holding elements
+// 8j..8j+7 of each half (16-byte accesses for bfloat16). The float32 arithmetic is fixed (no contraction into
 // fused multiply-adds, pairwise sums in a fixed tree, correctly rounded sqrt and
 // division) so the stored bytes are reproducible bit for bit:
 //   p_i  = x_i*x_i + x_{i+64}*x_{i+64}                      (i < 64)
@@ -25,26 +25,31 @@
 namespace qknr {
 namespace {
 
-template <typename T> struct Vec4;
-template <> struct Vec4<float> {
-  __device__ static void load(const float* p, float (&o)[4]) {
-    float4 v = *reinterpret_cast<const float4*>(p);
-    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+template <typename T> struct Vec8;
+template <> struct Vec8<float> {
+  __device__ static void load(const float* p, float (&o)[8]) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    const float4 v = *reinterpret_cast<const float4*>(p + 4);
+    o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w; o[4] = v.x; o[5] = v.y; o[6] = v.z; o[7] = v.w;
   }
-  __device__ static void store(float* p, const float (&o)[4]) {
+  __device__ static void store(float* p, const float (&o)[8]) {
     *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(o[4], o[5], o[6], o[7]);
   }
 };
-template <> struct Vec4<uint16_t> {
-  __device__ static void load(const uint16_t* p, float (&o)[4]) {
-    uint2 v = *reinterpret_cast<const uint2*>(p);
+template <> struct Vec8<uint16_t> {
+  __device__ static void load(const uint16_t* p, float (&o)[8]) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
     o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+    o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
   }
-  __device__ static void store(uint16_t* p, const float (&o)[4]) {
-    uint2 v;
+  __device__ static void store(uint16_t* p, const float (&o)[8]) {
+    uint4 v;
     v.x = f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16);
     v.y = f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16);
-    *reinterpret_cast<uint2*>(p) = v;
+    v.z = f32_to_bf16(o[4]) | (f32_to_bf16(o[5]) << 16);
+    v.w = f32_to_bf16(o[6]) | (f32_to_bf16(o[7]) << 16);
+    *reinterpret_cast<uint4*>(p) = v;
   }
 };
 
@@ -76,7 +81,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(
     TOut* __restrict__ q_out, TOut* __restrict__ k_pool, TOut* __restrict__ v_pool) {
   __shared__ float s_ss[WHOLE ? 2 : 1][WHOLE ? kMaxWholeHeads : 1];
   __shared__ float s_r[2];
-  __shared__ float s_y[PARTIAL ? 16 : 1][PARTIAL ? kHeadDim : 1];
+  __shared__ float s_y[PARTIAL ? 32 : 1][PARTIAL ? kHeadDim : 1];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int pos = positions[t];
@@ -96,13 +101,13 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(
   }
   if (slot >= pool_slots) slot = -1;
 
-  const int j = tid & 15;
-  const int grp = tid >> 4;
+  const int j = tid & 7;     // lane within the head vector's 8
+  const int grp = tid >> 3;  // 32 head vectors in flight
   const int half_r = PARTIAL ? rotary_dim / 2 : kHeadDim / 2;
-  float c[4], s[4];
+  float c[8], s[8];
   if (!PARTIAL) {
-    Vec4<float>::load(rope_cos + (int64_t)pos * (kHeadDim / 2) + 4 * j, c);
-    Vec4<float>::load(rope_sin + (int64_t)pos * (kHeadDim / 2) + 4 * j, s);
+    Vec8<float>::load(rope_cos + (int64_t)pos * (kHeadDim / 2) + 8 * j, c);
+    Vec8<float>::load(rope_sin + (int64_t)pos * (kHeadDim / 2) + 8 * j, s);
   }
   const float* cs_row = rope_cos + (int64_t)pos * half_r;
   const float* sn_row = rope_sin + (int64_t)pos * half_r;
@@ -112,25 +117,25 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(
     return hv < n_q_heads ? q + ((int64_t)t * n_q_heads + hv) * kHeadDim
                           : k + ((int64_t)t * n_kv_heads + (hv - n_q_heads)) * kHeadDim;
   };
-  // per-head sum of squares: lane j holds elements 4j..4j+3 of each half
-  auto head_ss = [&](const float (&a)[4], const float (&b)[4]) {
-    float p0 = a[0] * a[0] + b[0] * b[0];
-    float p1 = a[1] * a[1] + b[1] * b[1];
-    float p2 = a[2] * a[2] + b[2] * b[2];
-    float p3 = a[3] * a[3] + b[3] * b[3];
-    float ss = (p0 + p1) + (p2 + p3);
-    ss = ss + __shfl_xor(ss, 1, 16);
-    ss = ss + __shfl_xor(ss, 2, 16);
-    ss = ss + __shfl_xor(ss, 4, 16);
-    ss = ss + __shfl_xor(ss, 8, 16);
+  // per-head sum of squares: lane j holds elements 8j..8j+7 of each half; its
+  // in-lane adds are the first three levels of the pairwise tree over the 64
+  // p_i, the three xor-shuffles the rest
+  auto head_ss = [&](const float (&a)[8], const float (&b)[8]) {
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = a[i] * a[i] + b[i] * b[i];
+    float ss = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    ss = ss + __shfl_xor(ss, 1, 8);
+    ss = ss + __shfl_xor(ss, 2, 8);
+    ss = ss + __shfl_xor(ss, 4, 8);
     return ss;
   };
 
   if (WHOLE) {
-    for (int hv = grp; hv < n_norm; hv += 16) {
-      float a[4], b[4];
-      Vec4<TIn>::load(source(hv) + 4 * j, a);
-      Vec4<TIn>::load(source(hv) + kHeadDim / 2 + 4 * j, b);
+    for (int hv = grp; hv < n_norm; hv += 32) {
+      float a[8], b[8];
+      Vec8<TIn>::load(source(hv) + 8 * j, a);
+      Vec8<TIn>::load(source(hv) + kHeadDim / 2 + 8 * j, b);
       const float ss = head_ss(a, b);
       if (j == 0) {
         if (hv < n_q_heads) s_ss[0][hv] = ss;
@@ -147,7 +152,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(
     __syncthreads();
   }
 
-  for (int hv = grp; hv < n_norm; hv += 16) {
+  for (int hv = grp; hv < n_norm; hv += 32) {
     const TIn* src = source(hv);
     const float* g;
     TOut* dst;
@@ -164,9 +169,9 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(
       dst = k_pool + ((int64_t)hl * pool_slots + (write ? slot : 0)) * kHeadDim;
     }
     if (WHOLE) g += (int64_t)hl * kHeadDim;
-    float a[4], b[4];
-    Vec4<TIn>::load(src + 4 * j, a);
-    Vec4<TIn>::load(src + kHeadDim / 2 + 4 * j, b);
+    float a[8], b[8];
+    Vec8<TIn>::load(src + 8 * j, a);
+    Vec8<TIn>::load(src + kHeadDim / 2 + 8 * j, b);
 
     float r;
     if (WHOLE) {
@@ -176,19 +181,19 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(
       r = 1.0f / __builtin_sqrtf(ms + eps);
     }
 
-    float ga[4], gb[4];
-    Vec4<float>::load(g + 4 * j, ga);
-    Vec4<float>::load(g + kHeadDim / 2 + 4 * j, gb);
-    float ya[4], yb[4];
+    float ga[8], gb[8];
+    Vec8<float>::load(g + 8 * j, ga);
+    Vec8<float>::load(g + kHeadDim / 2 + 8 * j, gb);
+    float ya[8], yb[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       ya[i] = (a[i] * r) * ga[i];
       yb[i] = (b[i] * r) * gb[i];
     }
-    float oa[4], ob[4];
+    float oa[8], ob[8];
     if (!PARTIAL) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 8; ++i) {
         const float ac = ya[i] * c[i];
         const float bs = yb[i] * s[i];
         const float bc = yb[i] * c[i];
@@ -197,13 +202,13 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(
         ob[i] = bc + as;
       }
     } else {
-      // pairs (e, e + R/2) for e < R/2 may sit in other lanes of the 16: go through LDS
-      // (the 16 lanes of a head are one wave, so program order orders the accesses)
+      // pairs (e, e + R/2) for e < R/2 may sit in other lanes of the 8: go through LDS
+      // (the 8 lanes of a head are one wave, so program order orders the accesses)
       float* yrow = s_y[grp];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        yrow[4 * j + i] = ya[i];
-        yrow[kHeadDim / 2 + 4 * j + i] = yb[i];
+      for (int i = 0; i < 8; ++i) {
+        yrow[8 * j + i] = ya[i];
+        yrow[kHeadDim / 2 + 8 * j + i] = yb[i];
       }
       __builtin_amdgcn_wave_barrier();
       auto rot = [&](int e, float y) -> float {
@@ -221,26 +226,26 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(
         return y;
       };
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        oa[i] = rot(4 * j + i, ya[i]);
-        ob[i] = rot(kHeadDim / 2 + 4 * j + i, yb[i]);
+      for (int i = 0; i < 8; ++i) {
+        oa[i] = rot(8 * j + i, ya[i]);
+        ob[i] = rot(kHeadDim / 2 + 8 * j + i, yb[i]);
       }
       __builtin_amdgcn_wave_barrier();   // the row is rewritten by the group's next head
     }
     if (write) {
-      Vec4<TOut>::store(dst + 4 * j, oa);
-      Vec4<TOut>::store(dst + kHeadDim / 2 + 4 * j, ob);
+      Vec8<TOut>::store(dst + 8 * j, oa);
+      Vec8<TOut>::store(dst + kHeadDim / 2 + 8 * j, ob);
     }
   }
 
   if (slot >= 0) {
-    // v: cast only, 4 elements per thread per pass
-    for (int e = tid; e < n_kv_heads * (kHeadDim / 4); e += 256) {
-      const int kh = e / (kHeadDim / 4);
-      const int c4 = e % (kHeadDim / 4);
-      float x[4];
-      Vec4<TIn>::load(v + ((int64_t)t * n_kv_heads + kh) * kHeadDim + 4 * c4, x);
-      Vec4<TOut>::store(v_pool + ((int64_t)kh * pool_slots + slot) * kHeadDim + 4 * c4, x);
+    // v: cast only, 8 elements per thread per pass
+    for (int e = tid; e < n_kv_heads * (kHeadDim / 8); e += 256) {
+      const int kh = e / (kHeadDim / 8);
+      const int c8 = e % (kHeadDim / 8);
+      float x[8];
+      Vec8<TIn>::load(v + ((int64_t)t * n_kv_heads + kh) * kHeadDim + 8 * c8, x);
+      Vec8<TOut>::store(v_pool + ((int64_t)kh * pool_slots + slot) * kHeadDim + 8 * c8, x);
     }
   }
 }
