@@ -64,6 +64,24 @@ def algorithmic_work(w):
             "prefill_pairs": pre_pairs, "append_bytes": app_bytes}
 
 
+def measure_append_steady(Q, t, cos, sin, positions_all, q_out, k_pool, v_pool, P, R, stream, reps=50):
+    """The step's append, launched back to back after the timed region."""
+    import torch
+    def f():
+        Q.qknorm_rope_append(t["q"], t["k"], t["v"], t["q_gain"], t["k_gain"], cos, sin, positions_all,
+                             q_out, k_pool, v_pool, slots=t["slots"] if P else None,
+                             table=t["decode_table"] if R else None)
+    f()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        f()
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def measure_packed(Q, W, w, t, q_out, k_pool, v_pool, out, stream, reps=10):
     """The step's prompt tokens through packed_prefill_attn (each chunk its own
     prompt, attending only among itself), timed after the step's timed region."""
@@ -328,6 +346,7 @@ def main():
         times[k] /= args.steps  # ms per launch
     step_ms = sum(times.values())
 
+    app_steady_ms = measure_append_steady(Q, t, cos, sin, positions_all, q_out, k_pool, v_pool, P, R, stream)
     packed = measure_packed(Q, W, w, t, q_out, k_pool, v_pool, pre_out, stream) if P else None
     variants = measure_variants(Q, W, w, t, positions_all, q_out, k_pool, v_pool, dec_out, ws_d, stream)
 
@@ -364,7 +383,11 @@ def main():
                     "ms_per_launch": round(times["prefill"], 5), "bound": "mfma"},
         "append": {"gbs": round(app_gbs, 2), "frac": round(app_gbs / HBM_PEAK_GBS, 4),
                    "bytes_per_launch": work["append_bytes"], "ms_per_launch": round(times["append"], 5),
-                   "bound": "hbm"},
+                   "bound": "hbm",
+                   # the in-step events around this short kernel include the launch gap;
+                   # 50 back-to-back launches give the kernel's own rate
+                   "steady_gbs": round(work["append_bytes"] / (app_steady_ms * 1e-3) / 1e9, 2),
+                   "steady_ms_per_launch": round(app_steady_ms, 5)},
     }
     if packed is not None:
         result["packed_prefill"] = packed
