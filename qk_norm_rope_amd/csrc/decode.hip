@@ -58,8 +58,28 @@ struct DecodeParams {
 };
 
 // max over the 16 lanes of a DPP row, result in every lane of the row
-__device__ __forceinline__ float row_max16(float x) {
 #define QKNR_ROR(v, n) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + (n), 0xf, 0xf, false))
+
+// Sum over the 16 lanes of a row (every lane gets it): DPP rotations by 8, 4, 2, 1.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += QKNR_ROR(x, 8);
+  x += QKNR_ROR(x, 4);
+  x += QKNR_ROR(x, 2);
+  x += QKNR_ROR(x, 1);
+  return x;
+}
+
+// Sum of a lane's value over the four 16-lane groups (lanes l, l^16, l^32, l^48):
+// v_permlane16_swap pairs row 0 with row 1 and row 2 with row 3, v_permlane32_swap
+// the two halves.
+__device__ __forceinline__ float group_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, QKNR_ROR(x, 8));
   x = fmaxf(x, QKNR_ROR(x, 4));
   x = fmaxf(x, QKNR_ROR(x, 2));
@@ -277,18 +297,13 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(DecodeParams P) 
       }
     }
 
-    // ---- merge the wave's lanes, then the 4 waves
+    // ---- merge the wave's lanes (DPP rotations within 16 lanes, permlane swaps
+    // across the 16-lane groups: no LDS round trips), then the 4 waves
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
-      lsum[i] += __shfl_xor(lsum[i], 8, 16);
-      lsum[i] += __shfl_xor(lsum[i], 4, 16);
-      lsum[i] += __shfl_xor(lsum[i], 2, 16);
-      lsum[i] += __shfl_xor(lsum[i], 1, 16);
+      lsum[i] = row_sum16(lsum[i]);
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        acc[i][d] += __shfl_xor(acc[i][d], 16);
-        acc[i][d] += __shfl_xor(acc[i][d], 32);
-      }
+      for (int d = 0; d < 8; ++d) acc[i][d] = group_sum4(acc[i][d]);
     }
     if (l < 16) {
 #pragma unroll
