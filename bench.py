@@ -265,6 +265,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4, help="standard workload index (default: mixed step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measurements after the timed steps (packed form, variants, "
+                         "back-to-back append); for profiler runs that average per kernel name")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -346,9 +349,12 @@ def main():
         times[k] /= args.steps  # ms per launch
     step_ms = sum(times.values())
 
-    app_steady_ms = measure_append_steady(Q, t, cos, sin, positions_all, q_out, k_pool, v_pool, P, R, stream)
-    packed = measure_packed(Q, W, w, t, q_out, k_pool, v_pool, pre_out, stream) if P else None
-    variants = measure_variants(Q, W, w, t, positions_all, q_out, k_pool, v_pool, dec_out, ws_d, stream)
+    extras = not args.no_extras
+    app_steady_ms = measure_append_steady(Q, t, cos, sin, positions_all, q_out, k_pool, v_pool, P, R,
+                                          stream) if extras else None
+    packed = measure_packed(Q, W, w, t, q_out, k_pool, v_pool, pre_out, stream) if (P and extras) else None
+    variants = measure_variants(Q, W, w, t, positions_all, q_out, k_pool, v_pool, dec_out, ws_d,
+                                stream) if extras else None
 
     work = algorithmic_work(w)
     dec_gbs = work["decode_bytes"] / (times["decode"] * 1e-3) / 1e9 if R else 0.0
@@ -383,15 +389,17 @@ def main():
                     "ms_per_launch": round(times["prefill"], 5), "bound": "mfma"},
         "append": {"gbs": round(app_gbs, 2), "frac": round(app_gbs / HBM_PEAK_GBS, 4),
                    "bytes_per_launch": work["append_bytes"], "ms_per_launch": round(times["append"], 5),
-                   "bound": "hbm",
-                   # the in-step events around this short kernel include the launch gap;
-                   # 50 back-to-back launches give the kernel's own rate
-                   "steady_gbs": round(work["append_bytes"] / (app_steady_ms * 1e-3) / 1e9, 2),
-                   "steady_ms_per_launch": round(app_steady_ms, 5)},
+                   "bound": "hbm"},
     }
+    if app_steady_ms is not None:
+        # the in-step events around this short kernel include the launch gap;
+        # 50 back-to-back launches give the kernel's own rate
+        result["append"]["steady_gbs"] = round(work["append_bytes"] / (app_steady_ms * 1e-3) / 1e9, 2)
+        result["append"]["steady_ms_per_launch"] = round(app_steady_ms, 5)
     if packed is not None:
         result["packed_prefill"] = packed
-    result["variants"] = variants
+    if variants is not None:
+        result["variants"] = variants
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, snap)
     print(json.dumps(result), flush=True)
