@@ -268,6 +268,56 @@ int packed_prefill_attn_ex(void* stream, const qkr_pool* pool, int32_t n_tokens,
                            const qkr_attn_opts* opts);
 
 /*
+ * step_paged -- one mixed serving step in a single launch (nest
+ * "models/qwen3-8b/files": Entries table, step_paged; attention.linnet,
+ * step_paged): QK-norm + RoPE of the n_prefill prompt tokens and the n_decode
+ * decode rows, their k/v written into the pool, then prefill attention for the
+ * prompt tokens and decode attention for the rows, with every write before any
+ * read. The result is the one of
+ *   qknorm_rope_append over all n_prefill + n_decode tokens (slots for the
+ *     prompt tokens, table rows decode_row0 + b for decode row b), then
+ *   paged_prefill_attn over the prompt tokens and
+ *   paged_decode_attn over the rows (table + decode_row0 * pages_per_row):
+ * q_out and the pool bytes are identical to that sequence, prefill_out is
+ * identical to paged_prefill_attn's, and decode_out equals paged_decode_attn's
+ * up to float32 rounding (the page ranges are split differently).
+ *
+ * q, k, v: bfloat16 [n_prefill + n_decode][heads*head_dim], prompt tokens first
+ *   (in_dtype must be QKR_BF16, the pool bfloat16; else QKR_EUNSUPPORTED).
+ * positions, rows, slots: device int32 [n_prefill] (the prompt tokens);
+ * step_positions: device int32 [n_decode] (the decode rows).
+ * table: device int32 [n_table_rows][pages_per_row]; prompt token p uses row
+ *   rows[p], decode row b uses row decode_row0 + b (decode_row0 + n_decode <=
+ *   n_table_rows). At most 2048 pages per row and 8192 decode rows
+ *   (QKR_EUNSUPPORTED above).
+ * q_out: [n_prefill + n_decode][num_q_heads*head_dim] bfloat16;
+ * prefill_out: float32 [n_prefill][num_q_heads*head_dim];
+ * decode_out: float32 [n_decode][num_q_heads*head_dim].
+ * workspace: at least step_paged_workspace() bytes, zero-filled before its first
+ *   use; every call leaves it zero again (calls sharing it must be ordered on one
+ *   stream). Its int32 word 5 becomes 1 if a workgroup ever gave up waiting for
+ *   the writes (a wait bounded at one second that a correct launch never
+ *   exhausts; words 6 and 7 then hold the counts it saw); the library never
+ *   clears those words.
+ * Device indices are range-checked as in the three calls above.
+ *
+ * In this build the single-launch kernel is switched off: after the argument
+ * checks above, the call returns QKR_EUNSUPPORTED (qkr_last_error says so) and
+ * enqueues nothing. Use the three calls.
+ */
+int step_paged(void* stream, const qkr_pool* pool, int32_t n_prefill, int32_t n_decode,
+               const void* q, const void* k, const void* v, int32_t in_dtype,
+               const float* q_gain, const float* k_gain, float eps,
+               const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+               const int32_t* positions, const int32_t* rows, const int32_t* slots,
+               const int32_t* step_positions,
+               const int32_t* table, int32_t n_table_rows, int32_t pages_per_row, int32_t decode_row0,
+               float scale, void* q_out, void* k_pool, void* v_pool,
+               float* prefill_out, float* decode_out, void* workspace, size_t workspace_bytes);
+
+size_t step_paged_workspace(const qkr_pool* pool, int32_t n_prefill, int32_t n_decode, int32_t pages_per_row);
+
+/*
  * qkr_rope_table -- host helper: the RoPE cos/sin table (host memory).
  * For pos < rope_rows and i < head_dim/2:
  *   inv = 1 / theta^(2i/head_dim), a = pos*inv (double precision),

@@ -30,6 +30,8 @@ EXPORTED = (
     "packed_prefill_attn",
     "packed_prefill_attn_ex",
     "packed_prefill_attn_workspace",
+    "step_paged",
+    "step_paged_workspace",
     "qkr_rope_table",
     "qkr_status_str",
     "qkr_last_error",
@@ -110,6 +112,11 @@ def _load():
     lib.packed_prefill_attn.argtypes = [vp, pool_p, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, f32, vp, vp, sz]
     lib.packed_prefill_attn_workspace.restype = sz
     lib.packed_prefill_attn_workspace.argtypes = [pool_p, i32]
+    lib.step_paged.restype = ctypes.c_int
+    lib.step_paged.argtypes = [vp, pool_p, i32, i32, vp, vp, vp, i32, vp, vp, f32, vp, vp, i32,
+                               vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, sz]
+    lib.step_paged_workspace.restype = sz
+    lib.step_paged_workspace.argtypes = [pool_p, i32, i32, i32]
     lib.qkr_rope_table.restype = ctypes.c_int
     lib.qkr_rope_table.argtypes = [ctypes.c_double, i32, i32, vp, vp]
     lib.qkr_status_str.restype = ctypes.c_char_p
@@ -300,6 +307,45 @@ def packed_prefill_attn(q, k_pool, v_pool, table, rows, positions, segments, sca
         float(scale), _ptr(out, "out", torch.float32, n * n_q * HEAD_DIM),
         _ptr(workspace, "workspace"), ws_bytes, ctypes.byref(opts))
     _check(st, "packed_prefill_attn")
+
+
+def step_workspace_bytes(k_pool, num_q_heads: int, n_prefill: int, n_decode: int, pages_per_row: int) -> int:
+    pool = pool_desc(k_pool, num_q_heads)
+    return int(LIB.step_paged_workspace(ctypes.byref(pool), int(n_prefill), int(n_decode), int(pages_per_row)))
+
+
+def step_paged(q, k, v, q_gain, k_gain, rope_cos, rope_sin, positions, rows, slots, step_positions,
+               table, decode_row0: int, scale: float, q_out, k_pool, v_pool, prefill_out, decode_out,
+               workspace, eps: float = 1e-6, stream=None) -> None:
+    """One mixed step in a single launch: append over the prompt tokens (positions,
+    rows, slots) and the decode rows (step_positions, table rows decode_row0 + b),
+    then prefill attention into prefill_out and decode attention into decode_out."""
+    import torch
+    n_q = q_out.shape[-1] // HEAD_DIM
+    pool = pool_desc(k_pool, n_q)
+    P = 0 if positions is None else int(positions.numel())
+    R = 0 if step_positions is None else int(step_positions.numel())
+    n = P + R
+    ppr = int(table.shape[-1])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = LIB.step_paged(
+        _stream(stream), ctypes.byref(pool), P, R,
+        _ptr(q, "q", torch.bfloat16, n * n_q * HEAD_DIM), _ptr(k, "k", torch.bfloat16, n * pool.num_kv_heads * HEAD_DIM),
+        _ptr(v, "v", torch.bfloat16, n * pool.num_kv_heads * HEAD_DIM), _dtype_code(q),
+        _ptr(q_gain, "q_gain", torch.float32, HEAD_DIM), _ptr(k_gain, "k_gain", torch.float32, HEAD_DIM),
+        float(eps), _ptr(rope_cos, "rope_cos", torch.float32), _ptr(rope_sin, "rope_sin", torch.float32),
+        int(rope_cos.numel() // (HEAD_DIM // 2)),
+        _ptr(positions, "positions", torch.int32, P) if P else None,
+        _ptr(rows, "rows", torch.int32, P) if P else None,
+        _ptr(slots, "slots", torch.int32, P) if P else None,
+        _ptr(step_positions, "step_positions", torch.int32, R) if R else None,
+        _ptr(table, "table", torch.int32), int(table.shape[0]), ppr, int(decode_row0), float(scale),
+        _ptr(q_out, "q_out", torch.bfloat16, n * n_q * HEAD_DIM), _ptr(k_pool, "k_pool", torch.bfloat16),
+        _ptr(v_pool, "v_pool", torch.bfloat16),
+        _ptr(prefill_out, "prefill_out", torch.float32, P * n_q * HEAD_DIM) if P else None,
+        _ptr(decode_out, "decode_out", torch.float32, R * n_q * HEAD_DIM) if R else None,
+        _ptr(workspace, "workspace"), ws_bytes)
+    _check(st, "step_paged")
 
 
 def version() -> int:

@@ -32,6 +32,7 @@ SOURCES = {
     "decode.hip": [],
     "prefill.hip": [],
     "generic.hip": [],
+    "step.hip": [],
     "api.cpp": ["-ffp-contract=off"],
 }
 

@@ -295,4 +295,65 @@ int packed_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
                                 workspace_bytes, nullptr);
 }
 
+size_t step_paged_workspace(const qkr_pool* pool, int32_t n_prefill, int32_t n_decode, int32_t pages_per_row) {
+  if (check_pool(pool) != QKR_OK || n_prefill < 0 || n_decode < 0 || pages_per_row <= 0) return 0;
+  if (pool->dtype != QKR_BF16) return 0;
+  return qknr::step_workspace_bytes(n_prefill, n_decode, pool->num_kv_heads, pages_per_row);
+}
+
+int step_paged(void* stream, const qkr_pool* pool, int32_t n_prefill, int32_t n_decode,
+               const void* q, const void* k, const void* v, int32_t in_dtype,
+               const float* q_gain, const float* k_gain, float eps,
+               const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+               const int32_t* positions, const int32_t* rows, const int32_t* slots,
+               const int32_t* step_positions,
+               const int32_t* table, int32_t n_table_rows, int32_t pages_per_row, int32_t decode_row0,
+               float scale, void* q_out, void* k_pool, void* v_pool,
+               float* prefill_out, float* decode_out, void* workspace, size_t workspace_bytes) {
+  int st = check_pool(pool);
+  if (st != QKR_OK) return st;
+  if (n_prefill < 0 || n_decode < 0) return QKR_EINVAL;
+  if (in_dtype != QKR_F32 && in_dtype != QKR_BF16) return QKR_EUNSUPPORTED;
+  if (pool->dtype != QKR_BF16 || in_dtype != QKR_BF16) return QKR_EUNSUPPORTED;
+  if (n_prefill == 0 && n_decode == 0) return QKR_OK;
+  if ((int64_t)n_prefill + n_decode > (int64_t)1 << 30) return QKR_EUNSUPPORTED;
+  if (!q || !k || !v || !q_gain || !k_gain || !rope_cos || !rope_sin || !table || !q_out || !k_pool ||
+      !v_pool)
+    return QKR_EINVAL;
+  if (rope_rows <= 0 || n_table_rows <= 0 || pages_per_row <= 0) return QKR_EINVAL;
+  if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(scale)) return QKR_EINVAL;
+  if (n_prefill > 0 && (!positions || !rows || !slots || !prefill_out)) return QKR_EINVAL;
+  if (n_decode > 0) {
+    if (!step_positions || !decode_out) return QKR_EINVAL;
+    if (decode_row0 < 0 || (int64_t)decode_row0 + n_decode > n_table_rows) return QKR_EINVAL;
+    if (n_decode > qknr::step_max_rows()) return QKR_EUNSUPPORTED;
+  }
+  if (pages_per_row > qknr::prefill_max_pages_per_row()) return QKR_EUNSUPPORTED;
+  const size_t need = qknr::step_workspace_bytes(n_prefill, n_decode, pool->num_kv_heads, pages_per_row);
+  if (!workspace || workspace_bytes < need) return QKR_EWORKSPACE;
+  if (!qknr::step_enabled()) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "step_paged: the single-launch kernel is switched off in this build; "
+             "call qknorm_rope_append, paged_prefill_attn and paged_decode_attn");
+    return QKR_EUNSUPPORTED;
+  }
+  qknr::StepArgs a;
+  a.n_prefill = n_prefill;
+  a.n_decode = n_decode;
+  a.n_q_heads = pool->num_q_heads;
+  a.n_kv_heads = pool->num_kv_heads;
+  a.q = q; a.k = k; a.v = v;
+  a.q_gain = q_gain; a.k_gain = k_gain; a.eps = eps;
+  a.rope_cos = rope_cos; a.rope_sin = rope_sin; a.rope_rows = rope_rows;
+  a.positions = positions; a.step_positions = step_positions; a.rows = rows; a.slots = slots;
+  a.table = table; a.n_table_rows = n_table_rows; a.pages_per_row = pages_per_row;
+  a.decode_row0 = n_decode > 0 ? decode_row0 : 0;
+  a.num_pages = pool->num_pages;
+  a.scale = scale;
+  a.q_out = q_out; a.k_pool = k_pool; a.v_pool = v_pool;
+  a.prefill_out = prefill_out; a.decode_out = decode_out;
+  a.workspace = workspace;
+  return launch_status(qknr::launch_step(static_cast<hipStream_t>(stream), a));
+}
+
 }  // extern "C"

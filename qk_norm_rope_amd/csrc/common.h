@@ -10,6 +10,8 @@ constexpr int kHeadDim = 128;   // nest qwen3-8b README: head dimension 128
 constexpr int kPageSize = 64;   // nest qwen3-8b Entries table: PageSize 64
 constexpr int kGroup = 4;       // query heads per KV head (32 / 8)
 
+constexpr float kLog2e = 1.4426950408889634f;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -1,405 +1,17 @@
-// K2: paged decode attention, bfloat16, split evenly over the GPU (stream-K
-// flash decoding).
-//
-// nest "models/qwen3-8b/files": Entries table (decode_paged: row b's positions lie
-// in the pages table[b] lists, pages of 64) and src/attention.linnet (decode_paged
-// calls paged_attention with scale rsqrt(head_dim); decode: every position up to
-// and including the query's is visible). fantasma "src/inference/model.zig",
-// fullAttentionForward: query head h reads KV head h / 4; scores scaled by
-// 1/sqrt(head_dim); max-subtracted softmax; weighted sum of V.
-//
-// Work list: unit = (row b, KV head g, page p of the row), ordered by row, then KV
-// head, then page; a "segment" is the run of units of one (b, g). The grid is the
-// number of workgroups the GPU holds at once, and workgroup i takes units
-// [i*U/G, (i+1)*U/G): every workgroup streams the same number of 32 KB K/V page
-// chunks, whatever the rows' lengths. A segment that lies inside one workgroup's
-// range is finished there; a segment cut by range ends yields one partial
-// softmax state (max, sum, acc) per workgroup touching it, and the last of them
-// to finish (ticket counter per segment) merges them in workgroup order, so the
-// result depends only on the positions, never on timing or on where pages sit.
-//
-// Inside a workgroup, wave w takes keys 16w..16w+15 of each page, so each page's
-// K and V are read once for the 4 query heads of the group:
-//   * scores of 4 heads x 16 keys: 4 x v_mfma_f32_16x16x32_bf16 (query rows 4..15
-//     are zero);
-//   * online softmax per head, row max by DPP rotations inside 16-lane rows;
-//   * P.V on the vector ALU, lane l holding 8 dimensions of 4 keys, the
-//     probabilities passed through LDS;
-//   * the next page's K/V loads are in flight while the current page computes.
-// Partial states travel through agent-coherent (sc1) stores and loads with an
-// explicit wait before the ticket, so no cache-wide write-back is needed.
+// K2 kernel and launcher: one workgroup of 4 waves per resident slot of the GPU,
+// each streaming an equal slice of the (row, KV head, page) units. The device
+// code (and its design) is in decode_body.h.
 #include <algorithm>
 
-#include "common.h"
+#include "decode_body.h"
 #include "kernels.h"
 
 namespace qknr {
 namespace {
 
-constexpr int kPartial = kGroup * (kHeadDim + 2);  // floats per partial: per head (m, l, acc[128])
-constexpr int kMaxGrid = 2048;                     // workgroups launched at most
-constexpr int kMaxRows = 12288;                    // rows per call (LDS prefix table)
-constexpr float kLog2e = 1.4426950408889634f;
-
-struct DecodeParams {
-  int n_rows, n_kv;
-  const uint16_t* q;
-  const uint16_t* k_pool;
-  const uint16_t* v_pool;
-  int64_t num_pages;
-  const int* table;
-  int pages_per_row;
-  const int* positions;
-  float scale_log2;
-  float* out;
-  int* counters;      // [n_rows * n_kv], zero between calls
-  float* partials;    // [grid][2][kPartial]
-  const uint16_t* gate;   // optional output gate [n_rows][n_q*128], bf16
-};
-
-// max over the 16 lanes of a DPP row, result in every lane of the row
-#define QKNR_ROR(v, n) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + (n), 0xf, 0xf, false))
-
-// Sum over the 16 lanes of a row (every lane gets it): DPP rotations by 8, 4, 2, 1.
-__device__ __forceinline__ float row_sum16(float x) {
-  x += QKNR_ROR(x, 8);
-  x += QKNR_ROR(x, 4);
-  x += QKNR_ROR(x, 2);
-  x += QKNR_ROR(x, 1);
-  return x;
-}
-
-// Sum of a lane's value over the four 16-lane groups (lanes l, l^16, l^32, l^48):
-// v_permlane16_swap pairs row 0 with row 1 and row 2 with row 3, v_permlane32_swap
-// the two halves.
-__device__ __forceinline__ float group_sum4(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-__device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, QKNR_ROR(x, 8));
-  x = fmaxf(x, QKNR_ROR(x, 4));
-  x = fmaxf(x, QKNR_ROR(x, 2));
-  x = fmaxf(x, QKNR_ROR(x, 1));
-#undef QKNR_ROR
-  return x;
-}
-
-__device__ __forceinline__ void store_sc1(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_sc1(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ long long range_begin(int i, long long U, int G) { return (long long)i * U / G; }
-
-// workgroup whose range holds unit u
-__device__ __forceinline__ int owner(long long u, long long U, int G) {
-  int i = (int)((u * G) / U);
-  while (i + 1 < G && range_begin(i + 1, U, G) <= u) ++i;
-  while (i > 0 && range_begin(i, U, G) > u) --i;
-  return i;
-}
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-struct PageRegs {
-  bf16x8 k[4];
-  uint4 v[4];
-  bool ok;
-};
-
 __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(DecodeParams P) {
   extern __shared__ int s_prefix[];   // [n_rows + 1]: units before row b
-  __shared__ __attribute__((aligned(16))) float s_p[4][16][kGroup];
-  __shared__ float s_m[4][kGroup], s_l[4][kGroup];
-  __shared__ __attribute__((aligned(16))) float s_acc[4][kGroup][kHeadDim];
-  __shared__ int s_scan[4];
-  __shared__ int s_last;
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int l = tid & 63;
-  const int hr = l & 15;   // MFMA row/column index within a 16-lane group
-  const int G4 = l >> 4;   // 16-lane group
-  const int n_q = P.n_kv * kGroup;
-  const int max_pos = P.pages_per_row * kPageSize;
-  const int n_rows = P.n_rows;
-
-  // ---- units per row, exclusive prefix over rows (blocked scan)
-  {
-    const int per = (n_rows + 255) / 256;
-    const int b0 = tid * per;
-    int local = 0;
-    for (int b = b0; b < min(b0 + per, n_rows); ++b) {
-      const int p = P.positions[b];
-      local += (p >= 0 && p < max_pos) ? (p / kPageSize + 1) * P.n_kv : 0;
-    }
-    int incl = local;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(incl, d);
-      if (l >= d) incl += y;
-    }
-    if (l == 63) s_scan[w] = incl;
-    __syncthreads();
-    int off = 0;
-    for (int ww = 0; ww < w; ++ww) off += s_scan[ww];
-    int run = off + incl - local;
-    for (int b = b0; b < min(b0 + per, n_rows); ++b) {
-      s_prefix[b] = run;
-      const int p = P.positions[b];
-      run += (p >= 0 && p < max_pos) ? (p / kPageSize + 1) * P.n_kv : 0;
-    }
-    if (tid == 255) s_prefix[n_rows] = off + incl;
-    __syncthreads();
-  }
-  const long long U = s_prefix[n_rows];
-  const int Gd = gridDim.x;
-  const int gi = blockIdx.x;
-  const long long u0 = range_begin(gi, U, Gd);
-  const long long u1 = range_begin(gi + 1, U, Gd);
-  if (u0 >= u1) return;
-
-  const int64_t pool_slots = P.num_pages * kPageSize;
-
-  // row holding u0: last b with prefix[b] <= u0
-  int b = 0;
-  {
-    int lo = 0, hi = n_rows - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= u0) lo = mid; else hi = mid - 1;
-    }
-    b = lo;
-  }
-
-  long long u = u0;
-  bool first_segment = true;
-  while (u < u1) {
-    while (s_prefix[b + 1] <= u) ++b;   // skip rows without units
-    const int pos = P.positions[b];
-    const int np = pos / kPageSize + 1;
-    const long long base = s_prefix[b];
-    const int g = (int)((u - base) / np);
-    const int p0 = (int)((u - base) % np);
-    const long long seg_begin = base + (long long)g * np;
-    const long long seg_end = seg_begin + np;
-    const long long stop = min(u1, seg_end);
-    const int pe = p0 + (int)(stop - u);
-    const bool whole = (p0 == 0) && (pe == np);
-
-    // query operand: rows 0..3 = heads 4g..4g+3; k-slot 8*G4+i of step st = dim 8*(4*st+G4)+i,
-    // so each K load of a step reads 64 contiguous bytes of every row
-    bf16x8 qa[4];
-    if (hr < kGroup) {
-      const uint16_t* qp = P.q + ((int64_t)b * n_q + g * kGroup + hr) * kHeadDim;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const bf16x8*>(qp + 8 * (4 * st + G4));
-    } else {
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qa[st][i] = (__bf16)0.0f;
-    }
-    const uint16_t* kbase = P.k_pool + (int64_t)g * pool_slots * kHeadDim;
-    const uint16_t* vbase = P.v_pool + (int64_t)g * pool_slots * kHeadDim;
-    const int* trow = P.table + (int64_t)b * P.pages_per_row;
-
-    float m[kGroup], lsum[kGroup], acc[kGroup][8];
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      m[i] = -INFINITY;
-      lsum[i] = 0.f;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[i][d] = 0.f;
-    }
-
-    auto fetch = [&](int p, PageRegs& r) {
-      const int64_t page = trow[p];
-      r.ok = page >= 0 && page < P.num_pages;
-      const int64_t pg = r.ok ? page : 0;
-      const uint16_t* krow = kbase + (pg * kPageSize + 16 * w + hr) * kHeadDim + 8 * G4;
-      const uint16_t* vrow = vbase + (pg * kPageSize + 16 * w + 4 * G4) * kHeadDim + 8 * hr;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) r.k[st] = *reinterpret_cast<const bf16x8*>(krow + 32 * st);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        // V rows are read whole and once: streaming (non-temporal) loads
-        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vrow + jj * kHeadDim));
-        r.v[jj] = make_uint4(x[0], x[1], x[2], x[3]);
-      }
-    };
-
-    auto compute = [&](int p, const PageRegs& r) {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < 4; ++st) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], r.k[st], sc, 0, 0, 0);
-      // lanes 0..15: sc[i] = score of head i with key p*64 + 16w + lane
-      const int key0 = p * kPageSize + 16 * w;
-      const bool kvalid = r.ok && key0 + hr <= pos;
-      float pr[kGroup];
-      bool any_change = false;
-      float corr[kGroup];
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        const float x = kvalid ? sc[i] * P.scale_log2 : -INFINITY;
-        const float pm = lane0(row_max16(x));
-        const float mn = fmaxf(m[i], pm);
-        corr[i] = (m[i] == mn) ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);
-        any_change |= (m[i] != mn);
-        const float ms = (mn == -INFINITY) ? 0.f : mn;
-        pr[i] = __builtin_amdgcn_exp2f(x - ms);
-        lsum[i] = lsum[i] * corr[i] + pr[i];
-        m[i] = mn;
-      }
-      if (l < 16) *reinterpret_cast<float4*>(&s_p[w][l][0]) = make_float4(pr[0], pr[1], pr[2], pr[3]);
-      __builtin_amdgcn_wave_barrier();
-      if (any_change) {
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i)
-#pragma unroll
-          for (int d = 0; d < 8; ++d) acc[i][d] *= corr[i];
-      }
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int kk = 4 * G4 + jj;
-        const bool vok = r.ok && key0 + kk <= pos;
-        const float4 ph = *reinterpret_cast<const float4*>(&s_p[w][kk][0]);
-        float vf[8];
-        vf[0] = bf16_lo(r.v[jj].x); vf[1] = bf16_hi(r.v[jj].x);
-        vf[2] = bf16_lo(r.v[jj].y); vf[3] = bf16_hi(r.v[jj].y);
-        vf[4] = bf16_lo(r.v[jj].z); vf[5] = bf16_hi(r.v[jj].z);
-        vf[6] = bf16_lo(r.v[jj].w); vf[7] = bf16_hi(r.v[jj].w);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          const float x = vok ? vf[d] : 0.f;
-          acc[0][d] += ph.x * x;
-          acc[1][d] += ph.y * x;
-          acc[2][d] += ph.z * x;
-          acc[3][d] += ph.w * x;
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-    };
-
-    {
-      PageRegs ra, rb;
-      fetch(p0, ra);
-      for (int p = p0; p < pe; p += 2) {
-        if (p + 1 < pe) fetch(p + 1, rb);
-        compute(p, ra);
-        if (p + 2 < pe) fetch(p + 2, ra);
-        if (p + 1 < pe) compute(p + 1, rb);
-      }
-    }
-
-    // ---- merge the wave's lanes (DPP rotations within 16 lanes, permlane swaps
-    // across the 16-lane groups: no LDS round trips), then the 4 waves
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      lsum[i] = row_sum16(lsum[i]);
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[i][d] = group_sum4(acc[i][d]);
-    }
-    if (l < 16) {
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        float4* dst = reinterpret_cast<float4*>(&s_acc[w][i][8 * l]);
-        dst[0] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-        dst[1] = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
-      }
-    }
-    if (l == 0) {
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) { s_m[w][i] = m[i]; s_l[w][i] = lsum[i]; }
-    }
-    __syncthreads();
-    const int hi = tid >> 6;          // head within the group
-    const int dd = 2 * (tid & 63);    // two dimensions per thread
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_m[ww][hi]);
-    float L = 0.f, A0 = 0.f, A1 = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float mw = s_m[ww][hi];
-      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      L += f * s_l[ww][hi];
-      A0 += f * s_acc[ww][hi][dd];
-      A1 += f * s_acc[ww][hi][dd + 1];
-    }
-    float* orow = P.out + ((int64_t)b * n_q + g * kGroup + hi) * kHeadDim + dd;
-    // output gate: out *= sigmoid(gate) at the same element
-    float g0 = 1.f, g1 = 1.f;
-    if (P.gate) {
-      const uint32_t gw = *reinterpret_cast<const uint32_t*>(P.gate + ((int64_t)b * n_q + g * kGroup + hi) * kHeadDim + dd);
-      g0 = sigmoidf(bf16_lo(gw));
-      g1 = sigmoidf(bf16_hi(gw));
-    }
-    if (whole) {
-      orow[0] = (A0 / L) * g0;
-      orow[1] = (A1 / L) * g1;
-    } else {
-      const int slot = first_segment ? 0 : 1;
-      float* part = P.partials + ((int64_t)gi * 2 + slot) * kPartial + hi * (kHeadDim + 2);
-      if ((tid & 63) == 0) { store_sc1(part, M); store_sc1(part + 1, L); }
-      store_sc1(part + 2 + dd, A0);
-      store_sc1(part + 3 + dd, A1);
-      __builtin_amdgcn_s_waitcnt(0);   // the partial is at the coherence point before the ticket
-      __syncthreads();
-      const int rg = b * P.n_kv + g;
-      const int i0 = owner(seg_begin, U, Gd);
-      const int i1 = owner(seg_end - 1, U, Gd);
-      // workgroups with an empty range (fewer units than workgroups) add no partial
-      int count = 0;
-      for (int i = i0; i <= i1; ++i) count += range_begin(i, U, Gd) < range_begin(i + 1, U, Gd);
-      if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(&P.counters[rg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old == count - 1);
-      }
-      __syncthreads();
-      if (s_last) {
-        // one pass over the partials in workgroup order, 8 partials' loads in flight at a time
-        const bool i0_first = range_begin(i0, U, Gd) >= seg_begin;
-        float Mx = -INFINITY, Lt = 0.f, B0 = 0.f, B1 = 0.f;
-        for (int ib = i0; ib <= i1; ib += 8) {
-          float mv[8], lv[8], x0[8], x1[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int i = ib + k;
-            const bool ok = i <= i1 && range_begin(i, U, Gd) < range_begin(i + 1, U, Gd);
-            const int slot = (i == i0 && !i0_first) ? 1 : 0;
-            const float* ps = P.partials + ((int64_t)(ok ? i : i0) * 2 + slot) * kPartial + hi * (kHeadDim + 2);
-            mv[k] = ok ? load_sc1(ps) : -INFINITY;
-            lv[k] = ok ? load_sc1(ps + 1) : 0.f;
-            x0[k] = ok ? load_sc1(ps + 2 + dd) : 0.f;
-            x1[k] = ok ? load_sc1(ps + 3 + dd) : 0.f;
-          }
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            if (mv[k] == -INFINITY) continue;
-            const float mn = fmaxf(Mx, mv[k]);
-            const float fo = (Mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mx - mn);
-            const float fi = __builtin_amdgcn_exp2f(mv[k] - mn);
-            Lt = Lt * fo + lv[k] * fi;
-            B0 = B0 * fo + x0[k] * fi;
-            B1 = B1 * fo + x1[k] * fi;
-            Mx = mn;
-          }
-        }
-        orow[0] = (B0 / Lt) * g0;
-        orow[1] = (B1 / Lt) * g1;
-        if (tid == 0) __hip_atomic_store(&P.counters[rg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();   // LDS reuse by the next segment
-    first_segment = false;
-    u = stop;
-  }
+  decode_slice<4>(P, blockIdx.x, gridDim.x, s_prefix, threadIdx.x);
 }
 
 int grid_for_device() {

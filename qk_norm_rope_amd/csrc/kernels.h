@@ -69,4 +69,29 @@ hipError_t launch_segment_start(hipStream_t stream, int n_tokens, const int32_t*
 // visible positions.
 hipError_t launch_attention_generic(hipStream_t stream, const AttnArgs& a);
 
+// Single-launch mixed step: append over the prompt tokens and the decode rows,
+// then prefill attention over the prompt tokens and decode attention over the rows,
+// in one persistent kernel (bfloat16 inputs and pool).
+struct StepArgs {
+  int n_prefill, n_decode, n_q_heads, n_kv_heads;
+  const void *q, *k, *v;
+  const float *q_gain, *k_gain;
+  float eps;
+  const float *rope_cos, *rope_sin;
+  int rope_rows;
+  const int32_t *positions, *step_positions, *rows, *slots, *table;
+  int n_table_rows, pages_per_row, decode_row0;
+  int64_t num_pages;
+  float scale;
+  void *q_out, *k_pool, *v_pool;
+  float *prefill_out, *decode_out;
+  void* workspace;
+  int decode_slices = 0;   // decode work items (0: twice the resident workgroups)
+};
+size_t step_workspace_bytes(int n_prefill, int n_decode, int n_kv_heads, int pages_per_row);
+// Whether step_paged launches its kernel (off until the kernel has passed its GPU tests).
+bool step_enabled();
+int step_max_rows();
+hipError_t launch_step(hipStream_t stream, const StepArgs& a);
+
 }  // namespace qknr

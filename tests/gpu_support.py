@@ -116,18 +116,44 @@ class Run:
         Q.paged_decode_attn(self.q_out[P:], self.k_pool, self.v_pool, t["decode_table"],
                             t["step_positions"], W.SCALE, self.dec_out, workspace)
 
-    def step(self):
+    def fused_step(self, workspace=None):
+        """The whole step through step_paged (one launch)."""
+        Q = lib()
+        w, t = self.w, self.t
+        cos, sin = rope_tables()
+        P, R = w.n_prefill, w.n_decode
+        n_q = W.NUM_Q_HEADS * W.HEAD_DIM
+        self.q_out = torch.empty((w.n_tokens, n_q), dtype=self.td, device=DEV)
+        self.pre_out = torch.empty((P, n_q), dtype=torch.float32, device=DEV)
+        self.dec_out = torch.empty((R, n_q), dtype=torch.float32, device=DEV)
+        if workspace is None:
+            workspace = step_workspace(self.k_pool, P, R, w.pages_per_row)
+        Q.step_paged(t["q"], t["k"], t["v"], t["q_gain"], t["k_gain"], cos, sin,
+                     t["positions"] if P else None, t["rows"] if P else None, t["slots"] if P else None,
+                     t["step_positions"] if R else None, t["table"], w.decode_row0, W.SCALE,
+                     self.q_out, self.k_pool, self.v_pool, self.pre_out, self.dec_out, workspace)
+
+    def step_nosync(self):
         self.append()
         if self.w.n_prefill:
             self.prefill()
         if self.w.n_decode:
             self.decode()
+
+    def step(self):
+        self.step_nosync()
         torch.cuda.synchronize()
 
 
 def decode_workspace(k_pool, n_rows, pages_per_row):
     Q = lib()
     n = Q.decode_workspace_bytes(k_pool, W.NUM_Q_HEADS, n_rows, pages_per_row)
+    return torch.zeros(max(1, n), dtype=torch.uint8, device=DEV)
+
+
+def step_workspace(k_pool, n_prefill, n_decode, pages_per_row):
+    Q = lib()
+    n = Q.step_workspace_bytes(k_pool, W.NUM_Q_HEADS, n_prefill, n_decode, pages_per_row)
     return torch.zeros(max(1, n), dtype=torch.uint8, device=DEV)
 
 

@@ -173,3 +173,47 @@ def test_rope_table_rejects_bad_arguments():
     assert L.LIB.qkr_rope_table(1e6, 1, 3, p, p) == -1
     assert L.LIB.qkr_rope_table(-1.0, 1, 8, p, p) == -1
     assert L.LIB.qkr_rope_table(1e6, 1, 8, None, p) == -1
+
+
+def _step(pool, **kw):
+    args = dict(P=100, R=2, q=FAKE, k=FAKE, v=FAKE, in_dtype=L.QKR_BF16, qg=FAKE, kg=FAKE, eps=1e-6,
+                cos=FAKE, sin=FAKE, rope_rows=100, pos=FAKE, rows=FAKE, slots=FAKE, spos=FAKE, table=FAKE,
+                n_table_rows=4, ppr=4, row0=2, scale=0.1, q_out=FAKE, kp=FAKE, vp=FAKE, pout=FAKE, dout=FAKE,
+                ws=FAKE, ws_bytes=1 << 24)
+    args.update(kw)
+    a = args
+    return L.LIB.step_paged(None, ctypes.byref(pool), a["P"], a["R"], a["q"], a["k"], a["v"], a["in_dtype"],
+                            a["qg"], a["kg"], a["eps"], a["cos"], a["sin"], a["rope_rows"], a["pos"],
+                            a["rows"], a["slots"], a["spos"], a["table"], a["n_table_rows"], a["ppr"],
+                            a["row0"], a["scale"], a["q_out"], a["kp"], a["vp"], a["pout"], a["dout"],
+                            a["ws"], a["ws_bytes"])
+
+
+def test_step_host_checks():
+    pool = _pool()
+    assert _step(pool, P=0, R=0) == 0                                   # empty step: no-op
+    assert _step(_pool(dtype=L.QKR_F32)) == -2                          # bfloat16 pools only
+    assert _step(pool, in_dtype=L.QKR_F32) == -2                        # bfloat16 inputs only
+    assert _step(pool, P=-1) == -1
+    assert _step(pool, table=None) == -1
+    assert _step(pool, rows=None) == -1                                 # prompt tokens need rows
+    assert _step(pool, spos=None) == -1                                 # decode rows need positions
+    assert _step(pool, row0=3) == -1                                    # rows 3..4 of a 4-row table
+    assert _step(pool, row0=-1) == -1
+    assert _step(pool, scale=float("nan")) == -1
+    assert _step(pool, R=8193, n_table_rows=9000, row0=0) == -2        # decode rows per step
+    assert _step(pool, ppr=4096) == -2                                  # pages per row
+    need = L.LIB.step_paged_workspace(ctypes.byref(pool), 100, 2, 4)
+    assert need >= 64 * 4 + L.LIB.paged_decode_attn_workspace(ctypes.byref(pool), 2, 4)
+    assert _step(pool, ws_bytes=need - 1) == -3
+    assert _step(pool, ws=None, ws_bytes=need) == -3
+    assert L.LIB.step_paged_workspace(ctypes.byref(_pool(dtype=L.QKR_F32)), 100, 2, 4) == 0
+    assert L.LIB.step_paged_workspace(ctypes.byref(pool), 100, 0, 4) < need
+
+
+def test_step_is_switched_off_after_its_checks():
+    # valid arguments reach the switch: nothing is enqueued, the status says unsupported
+    pool = _pool()
+    need = L.LIB.step_paged_workspace(ctypes.byref(pool), 100, 2, 4)
+    assert _step(pool, ws_bytes=need) == -2
+    assert "switched off" in L.last_error()
