@@ -31,16 +31,25 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_2x2048_plus_128rows_hbm_traffic.txt")
+DECODE_SOURCES = ("decode.hip", "decode_body.h", "common.h")
 
 
-def measured_traffic(kernel: str, source: str):
-    """HBM bytes per launch from the committed counter summary, or None when the
-    kernel's source has changed since the counters were taken."""
+def sources_sha256(sources) -> str:
+    """sha256 over the named csrc files, in order (a kernel, its device code, helpers)."""
     import hashlib
+    h = hashlib.sha256()
+    for s in sources:
+        h.update(open(os.path.join(ROOT, "qk_norm_rope_amd", "csrc", s), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, sources):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel's sources have changed since the counters were taken."""
     try:
         kv = dict(line.split(": ", 1) for line in open(TRAFFIC_FILE).read().splitlines()
                   if line and not line.startswith("#"))
-        sha = hashlib.sha256(open(os.path.join(ROOT, "qk_norm_rope_amd", "csrc", source), "rb").read()).hexdigest()
+        sha = sources_sha256(sources)
         if kv.get(f"{kernel}.source_sha256") != sha:
             return None
         return int(float(kv[f"{kernel}.traffic_bytes_per_launch"]))
@@ -381,7 +390,7 @@ def main():
                    "head_dim": 128},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("paged_decode_bf16_kernel", "decode.hip") if args.workload == 4 else None,
+                     "traffic": measured_traffic("paged_decode_bf16_kernel", DECODE_SOURCES) if args.workload == 4 else None,
                      "kernel": "paged_decode_bf16_kernel",
                      "bytes_per_launch": work["decode_bytes"], "ms_per_launch": round(times["decode"], 5)},
         "prefill": {"tflops": round(pre_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,

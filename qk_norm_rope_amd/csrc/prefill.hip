@@ -18,13 +18,12 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(int n_tokens, const 
 // themselves (nest "models/qwen3-8b/files", src/attention.linnet prefill_packed:
 // token i sees token j when segments agree and positions[j] <= positions[i]). Each
 // segment is one run of the pack with positions rising by one, so the first visible
-// position is the position of the run's first token. One workgroup: a chunk of
-// tokens per thread, run starts carried across chunks by a prefix max.
-__global__ __launch_bounds__(1024) void segment_start_kernel(int n_tokens, const int* __restrict__ positions,
-                                                             const int* __restrict__ segments,
-                                                             int* __restrict__ lo) {
-  __shared__ int s_last[1024];
-  const int tid = threadIdx.x;
+// position is the position of the run's first token. One workgroup of 1024 threads:
+// a chunk of tokens per thread, run starts carried across chunks by a prefix max
+// (s_last: 1024 ints of LDS).
+__device__ __forceinline__ void segment_starts(int n_tokens, const int* __restrict__ positions,
+                                               const int* __restrict__ segments, int* __restrict__ lo,
+                                               int* s_last, int tid) {
   const int per = (n_tokens + 1023) / 1024;
   const int c0 = min(tid * per, n_tokens), c1 = min(c0 + per, n_tokens);
   int last = -1;   // index of the last run start inside this chunk
@@ -43,6 +42,26 @@ __global__ __launch_bounds__(1024) void segment_start_kernel(int n_tokens, const
     if (i == 0 || segments[i] != segments[i - 1]) start = i;
     lo[i] = min(positions[start], positions[i]);
   }
+}
+
+__global__ __launch_bounds__(1024) void segment_start_kernel(int n_tokens, const int* __restrict__ positions,
+                                                             const int* __restrict__ segments,
+                                                             int* __restrict__ lo) {
+  __shared__ int s_last[1024];
+  segment_starts(n_tokens, positions, segments, lo, s_last, threadIdx.x);
+}
+
+// The packed form's two set-up steps in one launch: first visible positions, then
+// the tile order by cost (the workgroup's own lo writes are visible to it after
+// the barrier).
+__global__ __launch_bounds__(1024) void packed_plan_kernel(int n_tokens, const int* __restrict__ positions,
+                                                           const int* __restrict__ segments, int* __restrict__ lo,
+                                                           int n_tiles, int* __restrict__ order) {
+  __shared__ int s_last[1024];
+  __shared__ unsigned long long keys[kPlanMaxTiles];
+  segment_starts(n_tokens, positions, segments, lo, s_last, threadIdx.x);
+  __syncthreads();
+  plan_tiles(n_tokens, positions, lo, n_tiles, order, keys, threadIdx.x, blockDim.x);
 }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
@@ -71,16 +90,20 @@ hipError_t launch_prefill_bf16(hipStream_t stream, const AttnArgs& a) {
   const int n_tiles = (a.n_queries + kTile - 1) / kTile;
   int* order = nullptr;
   int* lo = nullptr;
-  if (a.segments) {   // packed form: first visible positions after the tile order
+  if (a.segments)   // packed form: first visible positions after the tile order
     lo = reinterpret_cast<int*>(static_cast<char*>(a.workspace) + prefill_workspace_bytes(a.n_queries, a.n_kv_heads));
-    hipError_t e = launch_segment_start(stream, a.n_queries, a.positions, a.segments, lo);
-    if (e != hipSuccess) return e;
-  }
   if (n_tiles <= kPlanMaxTiles) {
     order = static_cast<int*>(a.workspace);
-    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, a.n_queries,
-                       a.positions, lo, n_tiles, order);
+    if (lo)
+      hipLaunchKernelGGL(packed_plan_kernel, dim3(1), dim3(1024), 0, stream, a.n_queries, a.positions,
+                         a.segments, lo, n_tiles, order);
+    else
+      hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, a.n_queries, a.positions,
+                         nullptr, n_tiles, order);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (lo) {
+    hipError_t e = launch_segment_start(stream, a.n_queries, a.positions, a.segments, lo);
     if (e != hipSuccess) return e;
   }
   PrefillParams P;

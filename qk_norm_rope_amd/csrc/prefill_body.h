@@ -50,23 +50,39 @@ __device__ __forceinline__ void plan_tiles(int n_tokens, const int* __restrict__
   int npow2 = 1;
   while (npow2 < n_tiles) npow2 <<= 1;
   // cost of a tile: keys from its smallest first visible position to its largest
-  // position; one wave per tile, one lane per token
+  // position; one wave per tile, one lane per token. A wave takes kBatch tiles at a
+  // time and issues all their loads before reducing, so a batch costs one memory
+  // round trip instead of one per tile.
+  constexpr int kBatch = 8;
   const int wave = tid >> 6, lane = tid & 63, n_waves = nthreads >> 6;
-  for (int i = wave; i < npow2; i += n_waves) {
-    int cost = 0;
-    if (i < n_tiles) {
+  const int* lsrc = lo ? lo : positions;   // read either way (no branch around the load)
+  for (int i0 = wave; i0 < npow2; i0 += kBatch * n_waves) {
+    int hi[kBatch], first[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {   // unconditional loads (clamped index), then selects
+      const int i = i0 + u * n_waves;
       const int t = i * kTile + lane;
-      int hi = t < n_tokens ? max(positions[t] + 1, 0) : 0;
-      int first = (t < n_tokens && lo) ? max(lo[t], 0) : (lo ? 0x7fffffff : 0);
+      const bool ok = i < n_tiles && t < n_tokens;
+      const int tc = ok ? t : 0;   // n_tokens >= 1
+      hi[u] = positions[tc];
+      first[u] = lsrc[tc];
+      hi[u] = ok ? max(hi[u] + 1, 0) : 0;
+      first[u] = lo ? (ok ? max(first[u], 0) : 0x7fffffff) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * n_waves;
+      if (i >= npow2) break;
+      int h = hi[u], f = first[u];
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) {
-        hi = max(hi, __shfl_xor(hi, m));
-        first = min(first, __shfl_xor(first, m));
+        h = max(h, __shfl_xor(h, m));
+        f = min(f, __shfl_xor(f, m));
       }
-      cost = max(hi - first, 0);
+      const int cost = max(h - f, 0);
+      if (lane == 0)
+        keys[i] = i < n_tiles ? ((unsigned long long)(0xffffffffu - (unsigned)cost) << 32) | (unsigned)i : ~0ull;
     }
-    if (lane == 0)
-      keys[i] = i < n_tiles ? ((unsigned long long)(0xffffffffu - (unsigned)cost) << 32) | (unsigned)i : ~0ull;
   }
   __syncthreads();
   for (int k = 2; k <= npow2; k <<= 1) {
