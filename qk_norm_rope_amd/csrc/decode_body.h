@@ -10,10 +10,10 @@
 // 1/sqrt(head_dim); max-subtracted softmax; weighted sum of V.
 //
 // Work list: unit = (row b, KV head g, page p of the row), ordered by row, then KV
-// head, then page; a "segment" is the run of units of one (b, g). The grid is the
-// number of workgroups the GPU holds at once, and workgroup i takes units
-// [i*U/G, (i+1)*U/G): every workgroup streams the same number of 32 KB K/V page
-// chunks, whatever the rows' lengths. A segment that lies inside one workgroup's
+// head, then page; a "segment" is the run of units of one (b, g). The grid G is
+// the number of workgroups the GPU holds at once (twice that for large batches),
+// and workgroup i takes units [i*U/G, (i+1)*U/G): every workgroup streams the same
+// number of 32 KB K/V page chunks, whatever the rows' lengths. A segment that lies inside one workgroup's
 // range is finished there; a segment cut by range ends yields one partial
 // softmax state (max, sum, acc) per workgroup touching it, and the last of them
 // to finish (ticket counter per segment) merges them in workgroup order, so the
