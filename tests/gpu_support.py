@@ -79,6 +79,7 @@ class Run:
         self.k_pre = self.k_pool.clone() if keep_pre else None
         self.v_pre = self.v_pool.clone() if keep_pre else None
         self.td = W.torch_dtype(w.dtype)
+        self.rope = None   # (cos, sin) device tables; None: rope_tables() (W.MAX_POSITIONS rows)
         self.q_out = None
         self.pre_out = None
         self.dec_out = None
@@ -89,7 +90,7 @@ class Run:
     def append(self):
         Q = lib()
         w, t = self.w, self.t
-        cos, sin = rope_tables()
+        cos, sin = self.rope or rope_tables()
         self.q_out = torch.empty((w.n_tokens, W.NUM_Q_HEADS * W.HEAD_DIM), dtype=self.td, device=DEV)
         Q.qknorm_rope_append(t["q"], t["k"], t["v"], t["q_gain"], t["k_gain"], cos, sin,
                              self.positions_all(), self.q_out, self.k_pool, self.v_pool,

@@ -217,3 +217,14 @@ def test_step_is_switched_off_after_its_checks():
     need = L.LIB.step_paged_workspace(ctypes.byref(pool), 100, 2, 4)
     assert _step(pool, ws_bytes=need) == -2
     assert "switched off" in L.last_error()
+
+
+def test_size_limits_host_checks():
+    pool = _pool()
+    lib = L.LIB
+    need = lib.paged_decode_attn_workspace(ctypes.byref(pool), 12289, 4)
+    assert lib.paged_decode_attn(None, ctypes.byref(pool), 12289, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+                                 0.1, FAKE, FAKE, need) == -2          # more rows than one call takes
+    pneed = lib.paged_prefill_attn_workspace(ctypes.byref(pool), 100)
+    assert lib.paged_prefill_attn(None, ctypes.byref(pool), 100, FAKE, FAKE, FAKE, FAKE, 3, 2049, FAKE,
+                                  FAKE, 0.1, FAKE, FAKE, pneed) == -2   # longer page table than prefill takes
