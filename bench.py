@@ -311,9 +311,12 @@ def main():
     ws_d = torch.zeros(max(1, Q.decode_workspace_bytes(k_pool, 32, max(R, 1), w.pages_per_row)),
                        dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    # four events per timed step (before the append, between the calls, after the
+    # decode); steps are issued back to back and read after one final sync
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
 
-    def step(timed):
+    def step(ev=None):
+        timed = ev is not None
         if timed:
             ev[0].record(stream)
         Q.qknorm_rope_append(t["q"], t["k"], t["v"], t["q_gain"], t["k_gain"], cos, sin, positions_all,
@@ -341,22 +344,22 @@ def main():
         del src, dst
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     times = {"append": 0.0, "prefill": 0.0, "decode": 0.0}
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-        # per-kernel windows come from the events of each step
-        ev[3].synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for ev in evs:   # per-kernel windows of each step
         times["append"] += ev[0].elapsed_time(ev[1])
         times["prefill"] += ev[1].elapsed_time(ev[2])
         times["decode"] += ev[2].elapsed_time(ev[3])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     for k in times:
         times[k] /= args.steps  # ms per launch
-    step_ms = sum(times.values())
+    # GPU time from the first step's start to the last step's end, per step
+    step_ms = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
 
     extras = not args.no_extras
     app_steady_ms = measure_append_steady(Q, t, cos, sin, positions_all, q_out, k_pool, v_pool, P, R,

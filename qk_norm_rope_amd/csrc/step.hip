@@ -64,15 +64,22 @@ struct StepParams {
   int* ctl;
 };
 
-// Thread 0 takes the ticket between two barriers, and the item number is read back
-// as a scalar. The leading barrier keeps thread 0's block that ends the previous
-// item (its release add) from being joined to this one across the loop's back
-// edge: with the two joined, the compiler built a loop nest in which only thread 0
-// left the inner loop to take tickets while the other threads of its wave went
-// around again on the old item, and the wave never let thread 0 run.
+// The single-thread steps of the loops (take a ticket, publish an item, wait, leave)
+// run in wave 0 under a scalar branch, with lane 0's value taken by readfirstlane,
+// never under a per-lane `tid == 0` branch: an earlier form with per-lane
+// branches was compiled into a loop nest in which only thread 0 left the inner
+// loop to take tickets, while the other threads of its wave went around again on
+// the old item and the wave never let thread 0 run (a hang). A barrier also
+// separates the publish step of one item from the ticket step of the next.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ int take_ticket(int* ctr, int* s_item) {
   __syncthreads();
-  if (threadIdx.x == 0) *s_item = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wave_id() == 0) {
+    const int old = __hip_atomic_fetch_add(ctr, (threadIdx.x & 63) == 0 ? 1 : 0, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    *s_item = __builtin_amdgcn_readfirstlane(old);   // lane 0's ticket, stored by every lane
+  }
   __syncthreads();
   const int it = __builtin_amdgcn_readfirstlane(*s_item);
   __syncthreads();   // s_item is rewritten by the next take
@@ -84,6 +91,8 @@ void step_paged_kernel(StepParams S) {
   extern __shared__ int s_prefix[];   // decode: [n_rows + 1]
   __shared__ int s_item;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const bool wave0 = wave_id() == 0;
   int* ctl = S.ctl;
 
   // ---- phase 1: the plan and the append items
@@ -108,18 +117,20 @@ void step_paged_kernel(StepParams S) {
     // publish: each wave's stores are complete, then one release by the workgroup
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0)
-      __hip_atomic_fetch_add(&ctl[it == 0 ? kPlanDone : kAppendDone], 1, __ATOMIC_RELEASE,
+    if (wave0)
+      __hip_atomic_fetch_add(&ctl[it == 0 ? kPlanDone : kAppendDone], lane == 0 ? 1 : 0, __ATOMIC_RELEASE,
                              __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- wait until every phase-1 item has published
-  if (tid == 0) {
+  if (wave0) {
     const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + kWaitTicks;
     int ready = 0, seen_a = 0, seen_p = 0;
     for (;;) {
-      seen_a = __hip_atomic_load(&ctl[kAppendDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      seen_p = __hip_atomic_load(&ctl[kPlanDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      seen_a = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(&ctl[kAppendDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      seen_p = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(&ctl[kPlanDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       if (seen_a >= S.n_append_items && seen_p >= 1) {
         ready = 1;
         break;
@@ -160,11 +171,11 @@ void step_paged_kernel(StepParams S) {
   }
 
   // ---- the last workgroup out clears the tickets (the fault words stay)
-  if (tid == 0) {
-    const int out = __hip_atomic_fetch_add(&ctl[kExited], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (out == (int)gridDim.x - 1) {
-      for (int i = kTicketA; i < kFault; ++i) __hip_atomic_store(&ctl[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+  if (wave0) {
+    const int out = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(
+        &ctl[kExited], lane == 0 ? 1 : 0, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT));
+    if (out == (int)gridDim.x - 1 && lane < kFault)   // lane i clears word i
+      __hip_atomic_store(&ctl[lane], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
