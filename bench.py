@@ -277,6 +277,10 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the measurements after the timed steps (packed form, variants, "
                          "back-to-back append); for profiler runs that average per kernel name")
+    ap.add_argument("--flush", action="store_true",
+                    help="before every timed step read a 1 GiB scratch buffer (evicts the 256 MB "
+                         "MALL and the L2 without leaving dirty lines), outside the timed windows; "
+                         "ms_per_step is then the sum of the windows")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -347,19 +351,28 @@ def main():
         step()
     torch.cuda.synchronize()
     times = {"append": 0.0, "prefill": 0.0, "decode": 0.0}
+    scratch = None
+    if args.flush:
+        scratch = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if scratch is not None:
+            scratch.amax()   # reads every byte, writes 4
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    del scratch
     for ev in evs:   # per-kernel windows of each step
         times["append"] += ev[0].elapsed_time(ev[1])
         times["prefill"] += ev[1].elapsed_time(ev[2])
         times["decode"] += ev[2].elapsed_time(ev[3])
     for k in times:
         times[k] /= args.steps  # ms per launch
-    # GPU time from the first step's start to the last step's end, per step
-    step_ms = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
+    # GPU time from the first step's start to the last step's end, per step (the sum
+    # of the windows when flushes run between the steps)
+    step_ms = (sum(times.values()) if args.flush
+               else evs[0][0].elapsed_time(evs[-1][3]) / args.steps)
 
     extras = not args.no_extras
     app_steady_ms = measure_append_steady(Q, t, cos, sin, positions_all, q_out, k_pool, v_pool, P, R,
@@ -390,7 +403,7 @@ def main():
                    "prefill_chunks": "2x2048 at positions 8192 and 0" if args.workload == 4 else None,
                    "decode_positions": "uniform [1, 16384]" if args.workload == 4 else None,
                    "pool_pages": w.num_pages, "page_size": 64, "q_heads": 32, "kv_heads": 8,
-                   "head_dim": 128},
+                   "head_dim": 128, "caches": "flushed before every step" if args.flush else "warm"},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("paged_decode_bf16_kernel", DECODE_SOURCES) if args.workload == 4 else None,
