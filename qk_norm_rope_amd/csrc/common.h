@@ -17,8 +17,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
 // float32 -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
@@ -30,12 +28,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 // low / high bfloat16 of a packed pair as float32
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
-}
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

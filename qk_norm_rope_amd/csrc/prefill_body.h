@@ -34,8 +34,6 @@ namespace qknr {
 namespace {
 
 constexpr int kTile = 64;
-constexpr int kKStride = kHeadDim + 8;    // bf16 per K row in LDS (16-byte reads, no conflicts)
-constexpr int kVStride = kHeadDim + 16;   // bf16 per V row in LDS (transposed 8-byte reads)
 constexpr int kPlanMaxTiles = 8192;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
