@@ -60,7 +60,7 @@ def measured_traffic(kernel: str, sources):
 def algorithmic_work(w):
     """Bytes / FLOPs each part of one step must move or compute."""
     import numpy as np
-    D, HQ, HKV = 128, 32, 8
+    D, HQ, HKV = 128, w.n_q_heads, w.n_kv_heads
     dec_pos = w.step_positions.astype(np.int64)
     R = len(dec_pos)
     dec_kv = int((dec_pos + 1).sum()) * HKV * D * 2 * 2          # K and V, bf16
@@ -98,7 +98,7 @@ def measure_packed(Q, W, w, t, q_out, k_pool, v_pool, out, stream, reps=10):
     import torch
     P = w.n_prefill
     seg = t["rows"]   # one prompt per chunk, one row per prompt
-    ws = torch.zeros(max(1, Q.packed_workspace_bytes(k_pool, 32, P)), dtype=torch.uint8, device=out.device)
+    ws = torch.zeros(max(1, Q.packed_workspace_bytes(k_pool, w.n_q_heads, P)), dtype=torch.uint8, device=out.device)
     for _ in range(2):
         Q.packed_prefill_attn(q_out[:P], k_pool, v_pool, t["table"], t["rows"], t["positions"], seg,
                               W.SCALE, out, ws)
@@ -117,7 +117,7 @@ def measure_packed(Q, W, w, t, q_out, k_pool, v_pool, out, stream, reps=10):
     for r, p in zip(rows, pos):
         first[r] = min(first.get(r, p), p)
     pairs = int(sum(p - first[r] + 1 for r, p in zip(rows, pos)))
-    flops = pairs * 4 * 128 * 32
+    flops = pairs * 4 * 128 * w.n_q_heads
     tf = flops / (ms * 1e-3) / 1e12
     return {"tflops": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "flops_per_launch": flops, "ms_per_launch": round(ms, 5), "bound": "mfma",
@@ -133,8 +133,8 @@ def measure_variants(Q, W, w, t, positions_all, q_out, k_pool, v_pool, dec_out, 
     dev = q_out.device
     work = algorithmic_work(w)
     rng = np.random.default_rng(7)
-    gq = torch.from_numpy(rng.uniform(0.5, 1.5, 32 * 128).astype(np.float32)).to(dev)
-    gk = torch.from_numpy(rng.uniform(0.5, 1.5, 8 * 128).astype(np.float32)).to(dev)
+    gq = torch.from_numpy(rng.uniform(0.5, 1.5, w.n_q_heads * 128).astype(np.float32)).to(dev)
+    gk = torch.from_numpy(rng.uniform(0.5, 1.5, w.n_kv_heads * 128).astype(np.float32)).to(dev)
     c64, s64 = Q.rope_table(1e6, W.MAX_POSITIONS, 64)
     c64, s64 = torch.from_numpy(c64).to(dev), torch.from_numpy(s64).to(dev)
     P, R = w.n_prefill, w.n_decode
@@ -158,10 +158,10 @@ def measure_variants(Q, W, w, t, positions_all, q_out, k_pool, v_pool, dec_out, 
     out = {"append_whole_norm_rotary64": {"gbs": round(work["append_bytes"] / (app_ms * 1e-3) / 1e9, 2),
                                           "ms_per_launch": round(app_ms, 5), "bound": "hbm"}}
     if R:
-        gate = torch.randn((R, 32 * 128), device=dev).to(torch.bfloat16)
+        gate = torch.randn((R, w.n_q_heads * 128), device=dev).to(torch.bfloat16)
         dec_ms = timed(lambda: Q.paged_decode_attn(q_out[P:], k_pool, v_pool, t["decode_table"],
                                                    t["step_positions"], W.SCALE, dec_out, ws_d, gate=gate))
-        gbs = (work["decode_bytes"] + R * 32 * 128 * 2) / (dec_ms * 1e-3) / 1e9
+        gbs = (work["decode_bytes"] + R * w.n_q_heads * 128 * 2) / (dec_ms * 1e-3) / 1e9
         out["decode_gated"] = {"gbs": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4),
                                "ms_per_launch": round(dec_ms, 5), "bound": "hbm"}
     return out
@@ -209,16 +209,17 @@ def cpu_baseline(w, snap, passes=4):
         cores = os.cpu_count() or 1
     rows, toks = snap["rows"], snap["toks"]
     P = w.n_prefill
+    heads = {"n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads}
     res = {"unit": "GB/s", "cores": int(cores), "kind": "oracle"}
     if rows:
         every_at = np.concatenate([w.positions, w.step_positions]).astype(np.int64)
         sel = [P + b for b in rows]
         q_out, k_rows, v_rows = O.append(w.q[sel], w.k[sel], w.v[sel], w.dtype, w.dtype,
-                                         w.q_gain, w.k_gain, every_at[sel])
+                                         w.q_gain, w.k_gain, every_at[sel], **heads)
         pos_s = w.step_positions[rows].astype(np.int64)
         ppr = -(-(int(pos_s.max()) + 1) // 64)
         table = np.arange(len(rows) * ppr, dtype=np.int32).reshape(len(rows), ppr)
-        kp = np.zeros((8, len(rows) * ppr * 64, 128), np.uint16)
+        kp = np.zeros((w.n_kv_heads, len(rows) * ppr * 64, 128), np.uint16)
         vp = np.zeros_like(kp)
         for i, b in enumerate(rows):
             n = int(pos_s[i])      # history positions 0..n-1, then the row's new token
@@ -228,22 +229,22 @@ def cpu_baseline(w, snap, passes=4):
             vp[:, base + n] = v_rows[i]
         t0 = time.perf_counter()
         for _ in range(passes):
-            O.decode(q_out, w.dtype, kp, vp, w.dtype, table, pos_s, W.SCALE)
+            O.decode(q_out, w.dtype, kp, vp, w.dtype, table, pos_s, W.SCALE, **heads)
         dt = (time.perf_counter() - t0) / passes
         del kp, vp
-        nbytes = int((pos_s + 1).sum()) * 8 * 128 * 2 * 2
+        nbytes = int((pos_s + 1).sum()) * w.n_kv_heads * 128 * 2 * 2
         res.update({"value": round(nbytes / dt / 1e9, 4), "seconds": round(dt * passes, 3),
                     "sample": f"float64 oracle decode of {len(rows)} of the {w.n_decode} decode rows "
                               f"({int((pos_s + 1).sum())} visible positions, {nbytes / 1e9:.3f} GB of K/V), "
                               f"{passes} passes"})
     if toks:
         q_pre, k_pre, v_pre = O.append(w.q[:P], w.k[:P], w.v[:P], w.dtype, w.dtype, w.q_gain,
-                                       w.k_gain, w.positions)
+                                       w.k_gain, w.positions, **heads)
         pre_rows = sorted(snap["pre"])
         nvis = {r: max(int(w.positions[t]) for t in toks if int(w.rows[t]) == r) + 1 for r in pre_rows}
         ppr2 = max(-(-n // 64) for n in nvis.values())
         tab2 = np.zeros((max(pre_rows) + 1, ppr2), np.int32)
-        kp2 = np.zeros((8, len(pre_rows) * ppr2 * 64, 128), np.uint16)
+        kp2 = np.zeros((w.n_kv_heads, len(pre_rows) * ppr2 * 64, 128), np.uint16)
         vp2 = np.zeros_like(kp2)
         for i, r in enumerate(pre_rows):
             base = i * ppr2 * 64
@@ -259,9 +260,9 @@ def cpu_baseline(w, snap, passes=4):
                 kp2[:, base + int(w.positions[t])] = k_pre[t]
                 vp2[:, base + int(w.positions[t])] = v_pre[t]
         t0 = time.perf_counter()
-        O.prefill(q_pre, w.dtype, kp2, vp2, w.dtype, tab2, w.rows, w.positions, W.SCALE, tokens=toks)
+        O.prefill(q_pre, w.dtype, kp2, vp2, w.dtype, tab2, w.rows, w.positions, W.SCALE, tokens=toks, **heads)
         dtp = time.perf_counter() - t0
-        flops = sum(int(w.positions[t]) + 1 for t in toks) * 4 * 128 * 32
+        flops = sum(int(w.positions[t]) + 1 for t in toks) * 4 * 128 * w.n_q_heads
         res["prefill"] = {"tflops": round(flops / dtp / 1e12, 6), "unit": "TFLOP/s", "seconds": round(dtp, 3),
                           "sample": f"float64 oracle prefill of {len(toks)} of the {P} prompt tokens"}
     return res
@@ -273,6 +274,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4, help="standard workload index (default: mixed step)")
+    ap.add_argument("--kv-heads", type=int, default=8, choices=(1, 2, 4, 8),
+                    help="KV heads of the workload (4 query heads each): 8 / S is one GPU's share "
+                         "when the heads are sharded over S GPUs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the measurements after the timed steps (packed form, variants, "
@@ -297,7 +301,7 @@ def main():
 
     dev = "cuda"
     torch.cuda.set_device(0)
-    w = W.config(args.workload)
+    w = W.config(args.workload, kv_heads=args.kv_heads)
     if w.dtype != "bf16":
         print("bench.py measures the bfloat16 workloads (1..4)", file=sys.stderr)
         sys.exit(2)
@@ -308,11 +312,12 @@ def main():
     cos, sin = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
     P, R = w.n_prefill, w.n_decode
     positions_all = torch.cat([t["positions"], t["step_positions"]])
-    q_out = torch.empty((P + R, 4096), dtype=torch.bfloat16, device=dev)
-    pre_out = torch.empty((max(P, 1), 4096), dtype=torch.float32, device=dev)
-    dec_out = torch.empty((max(R, 1), 4096), dtype=torch.float32, device=dev)
-    ws_p = torch.zeros(max(1, Q.prefill_workspace_bytes(k_pool, 32, max(P, 1))), dtype=torch.uint8, device=dev)
-    ws_d = torch.zeros(max(1, Q.decode_workspace_bytes(k_pool, 32, max(R, 1), w.pages_per_row)),
+    nq = w.n_q_heads * 128
+    q_out = torch.empty((P + R, nq), dtype=torch.bfloat16, device=dev)
+    pre_out = torch.empty((max(P, 1), nq), dtype=torch.float32, device=dev)
+    dec_out = torch.empty((max(R, 1), nq), dtype=torch.float32, device=dev)
+    ws_p = torch.zeros(max(1, Q.prefill_workspace_bytes(k_pool, w.n_q_heads, max(P, 1))), dtype=torch.uint8, device=dev)
+    ws_d = torch.zeros(max(1, Q.decode_workspace_bytes(k_pool, w.n_q_heads, max(R, 1), w.pages_per_row)),
                        dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     # four events per timed step (before the append, between the calls, after the
@@ -402,11 +407,12 @@ def main():
         "config": {"workload": w.name, "prefill_tokens": P, "decode_rows": R,
                    "prefill_chunks": "2x2048 at positions 8192 and 0" if args.workload == 4 else None,
                    "decode_positions": "uniform [1, 16384]" if args.workload == 4 else None,
-                   "pool_pages": w.num_pages, "page_size": 64, "q_heads": 32, "kv_heads": 8,
+                   "pool_pages": w.num_pages, "page_size": 64, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
                    "head_dim": 128, "caches": "flushed before every step" if args.flush else "warm"},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("paged_decode_bf16_kernel", DECODE_SOURCES) if args.workload == 4 else None,
+                     "traffic": measured_traffic("paged_decode_bf16_kernel", DECODE_SOURCES)
+                     if (args.workload == 4 and args.kv_heads == 8) else None,
                      "kernel": "paged_decode_bf16_kernel",
                      "bytes_per_launch": work["decode_bytes"], "ms_per_launch": round(times["decode"], 5)},
         "prefill": {"tflops": round(pre_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,

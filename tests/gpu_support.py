@@ -91,7 +91,7 @@ class Run:
         Q = lib()
         w, t = self.w, self.t
         cos, sin = self.rope or rope_tables()
-        self.q_out = torch.empty((w.n_tokens, W.NUM_Q_HEADS * W.HEAD_DIM), dtype=self.td, device=DEV)
+        self.q_out = torch.empty((w.n_tokens, w.n_q_heads * W.HEAD_DIM), dtype=self.td, device=DEV)
         Q.qknorm_rope_append(t["q"], t["k"], t["v"], t["q_gain"], t["k_gain"], cos, sin,
                              self.positions_all(), self.q_out, self.k_pool, self.v_pool,
                              slots=t["slots"] if w.n_prefill else None,
@@ -101,8 +101,8 @@ class Run:
         Q = lib()
         w, t = self.w, self.t
         P = w.n_prefill
-        self.pre_out = torch.empty((P, W.NUM_Q_HEADS * W.HEAD_DIM), dtype=torch.float32, device=DEV)
-        ws = torch.zeros(max(1, Q.prefill_workspace_bytes(self.k_pool, W.NUM_Q_HEADS, P)),
+        self.pre_out = torch.empty((P, w.n_q_heads * W.HEAD_DIM), dtype=torch.float32, device=DEV)
+        ws = torch.zeros(max(1, Q.prefill_workspace_bytes(self.k_pool, w.n_q_heads, P)),
                          dtype=torch.uint8, device=DEV)
         Q.paged_prefill_attn(self.q_out[:P], self.k_pool, self.v_pool, t["table"], t["rows"],
                              t["positions"], W.SCALE, self.pre_out, ws)
@@ -111,7 +111,7 @@ class Run:
         Q = lib()
         w, t = self.w, self.t
         P, R = w.n_prefill, w.n_decode
-        self.dec_out = torch.empty((R, W.NUM_Q_HEADS * W.HEAD_DIM), dtype=torch.float32, device=DEV)
+        self.dec_out = torch.empty((R, w.n_q_heads * W.HEAD_DIM), dtype=torch.float32, device=DEV)
         if workspace is None:
             workspace = decode_workspace(self.k_pool, R, w.pages_per_row)
         Q.paged_decode_attn(self.q_out[P:], self.k_pool, self.v_pool, t["decode_table"],
@@ -123,7 +123,7 @@ class Run:
         w, t = self.w, self.t
         cos, sin = rope_tables()
         P, R = w.n_prefill, w.n_decode
-        n_q = W.NUM_Q_HEADS * W.HEAD_DIM
+        n_q = w.n_q_heads * W.HEAD_DIM
         self.q_out = torch.empty((w.n_tokens, n_q), dtype=self.td, device=DEV)
         self.pre_out = torch.empty((P, n_q), dtype=torch.float32, device=DEV)
         self.dec_out = torch.empty((R, n_q), dtype=torch.float32, device=DEV)
@@ -148,13 +148,13 @@ class Run:
 
 def decode_workspace(k_pool, n_rows, pages_per_row):
     Q = lib()
-    n = Q.decode_workspace_bytes(k_pool, W.NUM_Q_HEADS, n_rows, pages_per_row)
+    n = Q.decode_workspace_bytes(k_pool, 4 * k_pool.shape[0], n_rows, pages_per_row)
     return torch.zeros(max(1, n), dtype=torch.uint8, device=DEV)
 
 
 def step_workspace(k_pool, n_prefill, n_decode, pages_per_row):
     Q = lib()
-    n = Q.step_workspace_bytes(k_pool, W.NUM_Q_HEADS, n_prefill, n_decode, pages_per_row)
+    n = Q.step_workspace_bytes(k_pool, 4 * k_pool.shape[0], n_prefill, n_decode, pages_per_row)
     return torch.zeros(max(1, n), dtype=torch.uint8, device=DEV)
 
 
@@ -163,7 +163,8 @@ def oracle_append(w: W.Workload):
     every_at = np.concatenate([w.positions, w.step_positions]).astype(np.int64)
     dec_slots = [O.page_slot(w.decode_table[b], int(w.step_positions[b])) for b in range(w.n_decode)]
     every_slot = np.concatenate([w.slots.astype(np.int64), np.asarray(dec_slots, dtype=np.int64)])
-    q_out, k_rows, v_rows = O.append(w.q, w.k, w.v, w.dtype, w.dtype, w.q_gain, w.k_gain, every_at)
+    q_out, k_rows, v_rows = O.append(w.q, w.k, w.v, w.dtype, w.dtype, w.q_gain, w.k_gain, every_at,
+                                     n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads)
     return q_out, k_rows, v_rows, every_slot
 
 
@@ -177,3 +178,22 @@ def max_abs_err(got: np.ndarray, ref: np.ndarray) -> float:
     assert got.shape == ref.shape
     assert np.isfinite(got).all(), "non-finite output"
     return float(np.max(np.abs(got.astype(np.float64) - ref)))
+
+
+def check_append(run, ref_q, k_rows, v_rows, slots):
+    """q_out bit-exact, and every pool byte: the written slots hold the oracle's
+    rows, all others their pre-step values (needs a Run with keep_pre)."""
+    w = run.w
+    assert np.array_equal(host_values(run.q_out, w.dtype), ref_q), "q_out bytes differ"
+    idx = torch.as_tensor(slots[slots >= 0], device=DEV)
+    td = run.td
+    keep = slots >= 0
+    for pool, pre, rows in ((run.k_pool, run.k_pre, k_rows), (run.v_pool, run.v_pre, v_rows)):
+        exp = pre
+        r = rows[keep]
+        if w.dtype == "bf16":
+            rt = torch.from_numpy(r.view(np.int16)).view(torch.bfloat16).to(DEV)
+        else:
+            rt = torch.from_numpy(r).to(DEV)
+        exp[:, idx] = rt.permute(1, 0, 2).to(td)
+        assert torch.equal(bits(pool), bits(exp)), "pool bytes differ"

@@ -13,7 +13,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_support import (DEV, TOL_BF16, TOL_F32, OraclePool, Run, bits, decode_workspace,
+from gpu_support import (DEV, TOL_BF16, TOL_F32, OraclePool, Run, bits, check_append, decode_workspace,
                          host_values, max_abs_err, oracle_append, oracle_pools)
 
 pytestmark = pytest.mark.gpu
@@ -40,23 +40,6 @@ def _sample(n, k, rng, must=()):
     return sorted(pick)
 
 
-def _check_append(run, ref_q, k_rows, v_rows, slots):
-    w = run.w
-    assert np.array_equal(host_values(run.q_out, w.dtype), ref_q), "q_out bytes differ"
-    idx = torch.as_tensor(slots[slots >= 0], device=DEV)
-    td = run.td
-    keep = slots >= 0
-    for pool, pre, rows in ((run.k_pool, run.k_pre, k_rows), (run.v_pool, run.v_pre, v_rows)):
-        exp = pre
-        r = rows[keep]
-        if w.dtype == "bf16":
-            rt = torch.from_numpy(r.view(np.int16)).view(torch.bfloat16).to(DEV)
-        else:
-            rt = torch.from_numpy(r).to(DEV)
-        exp[:, idx] = rt.permute(1, 0, 2).to(td)
-        assert torch.equal(bits(pool), bits(exp)), "pool bytes differ"
-
-
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_standard_workload(cfg):
     w = W.config(cfg)
@@ -64,7 +47,7 @@ def test_standard_workload(cfg):
     run = Run(w)
     run.step()
     ref_q, k_rows, v_rows, slots = oracle_append(w)
-    _check_append(run, ref_q, k_rows, v_rows, slots)
+    check_append(run, ref_q, k_rows, v_rows, slots)
     del run.k_pre, run.v_pre
     kp, vp = oracle_pools(w, k_rows, v_rows, slots)
     rng = np.random.default_rng(100 + cfg)
@@ -113,7 +96,7 @@ def test_ragged_decode_positions(dtype):
     run = Run(w)
     run.step()
     ref_q, k_rows, v_rows, slots = oracle_append(w)
-    _check_append(run, ref_q, k_rows, v_rows, slots)
+    check_append(run, ref_q, k_rows, v_rows, slots)
     kp, vp = oracle_pools(w, k_rows, v_rows, slots)
     ref = O.decode(ref_q, w.dtype, kp, vp, w.dtype, w.decode_table, w.step_positions, W.SCALE)
     err = max_abs_err(run.dec_out.cpu().numpy(), ref)
@@ -131,7 +114,7 @@ def test_ragged_prefill_chunks(dtype):
     run = Run(w)
     run.step()
     ref_q, k_rows, v_rows, slots = oracle_append(w)
-    _check_append(run, ref_q, k_rows, v_rows, slots)
+    check_append(run, ref_q, k_rows, v_rows, slots)
     kp, vp = oracle_pools(w, k_rows, v_rows, slots)
     ref = O.prefill(ref_q, w.dtype, kp, vp, w.dtype, w.table, w.rows, w.positions, W.SCALE)
     err = max_abs_err(run.pre_out.cpu().numpy(), ref)
@@ -146,7 +129,7 @@ def test_mixed_step_small():
     run = Run(w)
     run.step()
     ref_q, k_rows, v_rows, slots = oracle_append(w)
-    _check_append(run, ref_q, k_rows, v_rows, slots)
+    check_append(run, ref_q, k_rows, v_rows, slots)
     kp, vp = oracle_pools(w, k_rows, v_rows, slots)
     P = w.n_prefill
     ref_p = O.prefill(ref_q[:P], w.dtype, kp, vp, w.dtype, w.table, w.rows, w.positions, W.SCALE)
@@ -164,7 +147,7 @@ def test_negative_slot_skips_the_write():
     run.append()
     torch.cuda.synchronize()
     ref_q, k_rows, v_rows, slots = oracle_append(w)
-    _check_append(run, ref_q, k_rows, v_rows, slots)
+    check_append(run, ref_q, k_rows, v_rows, slots)
 
 
 def test_empty_batch_is_a_noop():

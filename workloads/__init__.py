@@ -66,7 +66,12 @@ class Workload:
     k_gain: np.ndarray             # float32 [128]
     history: list = field(default_factory=list)   # (row, n) : positions 0..n-1 pre-filled
     row_pages: dict = field(default_factory=dict)  # row -> allocated page ids, in order
+    n_kv_heads: int = NUM_KV_HEADS   # one GPU's share when the heads are sharded (8 / S)
     _history_slots: np.ndarray = field(default=None, repr=False)
+
+    @property
+    def n_q_heads(self) -> int:
+        return self.n_kv_heads * (NUM_Q_HEADS // NUM_KV_HEADS)
 
     @property
     def n_prefill(self) -> int:
@@ -111,7 +116,8 @@ def _bf16_bits(x: np.ndarray) -> np.ndarray:
 
 def build(name: str, seed: int, dtype: str, num_pages: int, pages_per_row: int,
           n_table_rows: int, chunks=(), decode=(), decode_row0: int = 0,
-          shared_prefix_pages: int = 0, reserve_page0: bool = True) -> Workload:
+          shared_prefix_pages: int = 0, reserve_page0: bool = True,
+          n_kv_heads: int = NUM_KV_HEADS) -> Workload:
     """General builder.
 
     ``chunks``: sequence of (row, first_position, length) prompt chunks, packed
@@ -119,6 +125,8 @@ def build(name: str, seed: int, dtype: str, num_pages: int, pages_per_row: int,
     ``decode``: sequence of (row, position); positions before it are history.
     ``shared_prefix_pages``: that many page ids are common to every row, and a
     row uses min(shared, position // 64) of them, so the page it writes is its own.
+    ``n_kv_heads``: KV heads of the workload (4 query heads each); fewer than 8 is
+    one GPU's share of the heads when they are sharded over 8 / n_kv_heads GPUs.
     """
     rng = np.random.default_rng(seed)
     need = {}      # row -> number of positions the row spans after the step
@@ -157,9 +165,10 @@ def build(name: str, seed: int, dtype: str, num_pages: int, pages_per_row: int,
         assert r == decode_row0 + b, "decode row b must use table row decode_row0 + b"
 
     n_tok = len(positions) + len(step_positions)
-    q = rng.standard_normal((n_tok, NUM_Q_HEADS * HEAD_DIM), dtype=np.float32)
-    k = rng.standard_normal((n_tok, NUM_KV_HEADS * HEAD_DIM), dtype=np.float32)
-    v = rng.standard_normal((n_tok, NUM_KV_HEADS * HEAD_DIM), dtype=np.float32)
+    n_q_heads = n_kv_heads * (NUM_Q_HEADS // NUM_KV_HEADS)
+    q = rng.standard_normal((n_tok, n_q_heads * HEAD_DIM), dtype=np.float32)
+    k = rng.standard_normal((n_tok, n_kv_heads * HEAD_DIM), dtype=np.float32)
+    v = rng.standard_normal((n_tok, n_kv_heads * HEAD_DIM), dtype=np.float32)
     q_gain = rng.uniform(0.5, 1.5, HEAD_DIM).astype(np.float32)
     k_gain = rng.uniform(0.5, 1.5, HEAD_DIM).astype(np.float32)
     if dtype == "bf16":
@@ -170,34 +179,36 @@ def build(name: str, seed: int, dtype: str, num_pages: int, pages_per_row: int,
         table=table, positions=np.asarray(positions, np.int32), rows=np.asarray(rows, np.int32),
         slots=np.asarray(slots, np.int32), step_positions=np.asarray(step_positions, np.int32),
         decode_row0=decode_row0, q=q, k=k, v=v, q_gain=q_gain, k_gain=k_gain,
-        history=history, row_pages=row_pages)
+        history=history, row_pages=row_pages, n_kv_heads=n_kv_heads)
 
 
-def config(i: int, seed: int | None = None) -> Workload:
-    """Standard workload ``i`` (0..4); the seed defaults to ``i``."""
+def config(i: int, seed: int | None = None, kv_heads: int = NUM_KV_HEADS) -> Workload:
+    """Standard workload ``i`` (0..4); the seed defaults to ``i``. ``kv_heads`` < 8
+    gives one GPU's share of it when the heads are sharded (same rows and positions)."""
     s = i if seed is None else seed
     rng = np.random.default_rng(10_000 + s)
-    name = CONFIG_NAMES[i]
+    name = CONFIG_NAMES[i] + ("" if kv_heads == NUM_KV_HEADS else f"_kv{kv_heads}")
+    kw = {"n_kv_heads": kv_heads}
     if i == 0:
         return build(name, s, "f32", num_pages=1, pages_per_row=1, n_table_rows=1,
-                     decode=[(0, 63)], reserve_page0=False)
+                     decode=[(0, 63)], reserve_page0=False, **kw)
     if i == 1:
         pos = rng.integers(256, 4096, size=8, endpoint=True)
         return build(name, s, "bf16", num_pages=1024, pages_per_row=65, n_table_rows=8,
-                     decode=[(b, int(p)) for b, p in enumerate(pos)])
+                     decode=[(b, int(p)) for b, p in enumerate(pos)], **kw)
     if i == 2:
         pos = np.floor(np.exp(rng.uniform(np.log(64), np.log(32768), size=64))).astype(int)
         return build(name, s, "bf16", num_pages=40960, pages_per_row=640, n_table_rows=64,
-                     decode=[(b, int(p)) for b, p in enumerate(pos)], shared_prefix_pages=8)
+                     decode=[(b, int(p)) for b, p in enumerate(pos)], shared_prefix_pages=8, **kw)
     if i == 3:
         lens = [512, 1024, 1000, 1560]
         return build(name, s, "bf16", num_pages=1024, pages_per_row=25, n_table_rows=4,
-                     chunks=[(r, 0, n) for r, n in enumerate(lens)])
+                     chunks=[(r, 0, n) for r, n in enumerate(lens)], **kw)
     if i == 4:
         pos = rng.integers(1, 16384, size=128, endpoint=True)
         return build(name, s, "bf16", num_pages=65536, pages_per_row=257, n_table_rows=130,
                      chunks=[(0, 8192, 2048), (1, 0, 2048)],
-                     decode=[(2 + b, int(p)) for b, p in enumerate(pos)], decode_row0=2)
+                     decode=[(2 + b, int(p)) for b, p in enumerate(pos)], decode_row0=2, **kw)
     raise IndexError(i)
 
 
@@ -239,17 +250,17 @@ def torch_dtype(dtype: str):
 
 
 def make_pools(w: Workload, device, chunk_slots: int = 1 << 16):
-    """K and V pools [8, num_pages*64, 128] on ``device`` holding the pre-step state."""
+    """K and V pools [n_kv_heads, num_pages*64, 128] on ``device`` holding the pre-step state."""
     import torch
     td = torch_dtype(w.dtype)
-    shape = (NUM_KV_HEADS, w.pool_slots, HEAD_DIM)
+    shape = (w.n_kv_heads, w.pool_slots, HEAD_DIM)
     k_pool = torch.full(shape, float("nan"), dtype=td, device=device)
     v_pool = torch.full(shape, float("nan"), dtype=td, device=device)
     hs = w.history_slots()
     for a in range(0, len(hs), chunk_slots):
         part = hs[a:a + chunk_slots]
         idx = torch.as_tensor(part, device=device)
-        for g in range(NUM_KV_HEADS):
+        for g in range(w.n_kv_heads):
             k_pool[g].index_copy_(0, idx, history_values(w.seed, 0, g, part, device).to(td))
             v_pool[g].index_copy_(0, idx, history_values(w.seed, 1, g, part, device).to(td))
     return k_pool, v_pool
