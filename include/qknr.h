@@ -215,8 +215,12 @@ int paged_decode_attn_ex(void* stream, const qkr_pool* pool, int32_t n_rows,
  * A bfloat16 pool takes tables of at most 2048 pages per row (131072 positions;
  * QKR_EUNSUPPORTED above).
  * out: float32 [n_tokens][num_q_heads*head_dim].
- * workspace: at least paged_prefill_attn_workspace() bytes (holds the tile
- * schedule); contents need no initialisation.
+ * workspace: at least paged_prefill_attn_workspace() bytes, sized for the
+ * current device (its CU count sets how many workgroups a long block's keys may
+ * be split over). It holds the block schedule and, for blocks whose keys are
+ * split, the partial softmax states and merge counters; contents need no
+ * initialisation (the call resets its counters). Calls that may overlap need
+ * workspaces of their own.
  */
 int paged_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
                        const void* q, const void* k_pool, const void* v_pool,
@@ -248,8 +252,8 @@ int paged_prefill_attn_ex(void* stream, const qkr_pool* pool, int32_t n_tokens,
  * of the pack whose positions rise by one, and all its tokens use one row.
  * segments: device int32 [n_tokens]; the other arguments as for
  * paged_prefill_attn (same row-length limit for a bfloat16 pool).
- * workspace: at least packed_prefill_attn_workspace() bytes; contents need no
- * initialisation.
+ * workspace: at least packed_prefill_attn_workspace() bytes; as for
+ * paged_prefill_attn, plus the tokens' first visible positions.
  */
 int packed_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
                         const void* q, const void* k_pool, const void* v_pool,

@@ -35,6 +35,15 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Agent-coherent float stores and loads (partial softmax states exchanged between
+// workgroups: visible across XCDs without a cache-wide write-back).
+__device__ __forceinline__ void store_sc1(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_sc1(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Logistic function 1 / (1 + e^-x): the attention output gate (fantasma
 // "src/inference/model.zig", fullAttentionForward: attn_out *= sigmoid(gate)).
 __device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }

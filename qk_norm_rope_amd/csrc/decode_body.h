@@ -86,13 +86,6 @@ __device__ __forceinline__ float row_max16(float x) {
   return x;
 }
 
-__device__ __forceinline__ void store_sc1(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_sc1(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ __forceinline__ long long range_begin(int i, long long U, int G) { return (long long)i * U / G; }
 
 // workgroup whose range holds unit u

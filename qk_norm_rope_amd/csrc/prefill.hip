@@ -1,18 +1,13 @@
 // K3 kernels and launchers: the tile plan, the first visible positions of a packed
 // form, and one workgroup per (64-token tile, KV head) work item. The device code
 // of a work item (and its design) is in prefill_body.h.
+#include <algorithm>
+
 #include "prefill_body.h"
 #include "kernels.h"
 
 namespace qknr {
 namespace {
-
-__global__ __launch_bounds__(1024) void prefill_plan_kernel(int n_tokens, const int* __restrict__ positions,
-                                                            const int* __restrict__ lo, int n_tiles,
-                                                            int* __restrict__ order) {
-  __shared__ unsigned long long keys[kPlanMaxTiles];
-  plan_tiles(n_tokens, positions, lo, n_tiles, order, keys, threadIdx.x, blockDim.x);
-}
 
 // First visible position of every token of a pack whose prompts attend only among
 // themselves (nest "models/qwen3-8b/files", src/attention.linnet prefill_packed:
@@ -51,17 +46,140 @@ __global__ __launch_bounds__(1024) void segment_start_kernel(int n_tokens, const
   segment_starts(n_tokens, positions, segments, lo, s_last, threadIdx.x);
 }
 
-// The packed form's two set-up steps in one launch: first visible positions, then
-// the tile order by cost (the workgroup's own lo writes are visible to it after
-// the barrier).
-__global__ __launch_bounds__(1024) void packed_plan_kernel(int n_tokens, const int* __restrict__ positions,
-                                                           const int* __restrict__ segments, int* __restrict__ lo,
-                                                           int n_tiles, int* __restrict__ order) {
-  __shared__ int s_last[1024];
-  __shared__ unsigned long long keys[kPlanMaxTiles];
-  segment_starts(n_tokens, positions, segments, lo, s_last, threadIdx.x);
+// Exclusive prefix sum of v over the 1024 threads of the workgroup (.x) and the
+// total (.y). s_scan: 16 ints of LDS; every thread calls it.
+__device__ int2 block_scan(int v, int* s_scan, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  __syncthreads();   // s_scan is free (a previous call's readers are done)
+  if (lane == 63) s_scan[wave] = x;
   __syncthreads();
-  plan_tiles(n_tokens, positions, lo, n_tiles, order, keys, threadIdx.x, blockDim.x);
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int c = s_scan[w];
+    before += w < wave ? c : 0;
+    total += c;
+  }
+  return make_int2(before + x - v, total);
+}
+
+constexpr int kSplitPlanMaxTiles = 512;   // tiles for which the plan considers key splits
+constexpr int kMinChunkPages = 4;          // pages of a chunk at least (a chunk's set-up is ~2 pages)
+
+// The work list of one prefill call (one workgroup of 1024 threads):
+//  1. the packed form's first visible positions (segments given);
+//  2. per tile: its key pages (from the smallest first visible position to the
+//     largest position), and whether its tokens form one run (one row, every
+//     index in range);
+//  3. tiles sorted by decreasing cost (largest visible span first);
+//  4. key splits (tiles <= kSplitPlanMaxTiles and a partial-state budget): with
+//     T = total item pages / CUs, a one-run tile of p > 1.5 T pages asks for
+//     min(8, ceil(p / T)) chunks; in the sorted order, a tile gets its chunks if
+//     the extra chunks asked for up to and including it fit the grid's spare
+//     workgroups; the chunks take the tile's place in the order. Every step is
+//     a block-wide sum or scan, one tile per thread.
+//     (A split costs a merge: partial states through memory, a release and an
+//     acquire that write back and invalidate the XCD's L2; below 1.5 T it loses.)
+//  5. the tickets of the split tiles' merges are zeroed.
+// Without splits the list is the sorted tiles, one pair each.
+__global__ __launch_bounds__(1024) void prefill_plan_kernel(
+    int n_tokens, const int* __restrict__ positions, const int* __restrict__ segments, int* __restrict__ lo,
+    const int* __restrict__ rows, int n_table_rows, int max_pos, int n_tiles, int n_kv, int n_cus,
+    int max_extra_pairs, int* __restrict__ n_pairs, int4* __restrict__ pairs, int* __restrict__ tickets) {
+  __shared__ unsigned long long keys[kPlanMaxTiles];
+  __shared__ int s_aux[kPlanMaxTiles];   // pages << 1 | one-run flag
+  __shared__ int s_last[1024];
+  __shared__ int s_scan[16];
+  const int tid = threadIdx.x;
+  if (segments) {
+    segment_starts(n_tokens, positions, segments, lo, s_last, tid);
+    __syncthreads();   // the workgroup's own lo writes are visible to it after the barrier
+  }
+  int npow2 = 1;
+  while (npow2 < n_tiles) npow2 <<= 1;
+  constexpr int kBatch = 8;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int* lsrc = lo ? lo : positions;
+  for (int i0 = wave; i0 < npow2; i0 += kBatch * 16) {
+    int pos[kBatch], fst[kBatch], row[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {   // every load of the batch first
+      const int i = i0 + u * 16;
+      const int t = i * kTile + lane;
+      const int tc = (i < n_tiles && t < n_tokens) ? t : 0;
+      pos[u] = positions[tc];
+      fst[u] = lsrc[tc];
+      row[u] = rows[tc];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * 16;
+      if (i >= npow2) break;
+      const int t = i * kTile + lane;
+      const bool ok = i < n_tiles && t < n_tokens;
+      int hi = ok ? max(pos[u] + 1, 0) : 0;
+      int f = lo ? (ok ? max(fst[u], 0) : 0x7fffffff) : 0;
+      const bool valid = !ok || (row[u] >= 0 && row[u] < n_table_rows && pos[u] >= 0 && pos[u] < max_pos);
+      int rmin = ok ? row[u] : 0x7fffffff, rmax = ok ? row[u] : -1;
+      const bool all_valid = __all(valid);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        hi = max(hi, __shfl_xor(hi, m));
+        f = min(f, __shfl_xor(f, m));
+        rmin = min(rmin, __shfl_xor(rmin, m));
+        rmax = max(rmax, __shfl_xor(rmax, m));
+      }
+      if (lane == 0 && i < npow2) {
+        const int cost = max(hi - f, 0);
+        keys[i] = i < n_tiles ? ((unsigned long long)(0xffffffffu - (unsigned)cost) << 32) | (unsigned)i : ~0ull;
+        const int pages = hi > f ? (hi - 1) / kPageSize - f / kPageSize + 1 : 0;
+        s_aux[i] = (pages << 1) | ((all_valid && rmin == rmax) ? 1 : 0);
+      }
+    }
+  }
+  __syncthreads();
+  for (int k = 2; k <= npow2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < npow2; i += 1024) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long a = keys[i], b = keys[ixj];
+          const bool up = (i & k) == 0;
+          if ((a > b) == up) { keys[i] = b; keys[ixj] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (max_extra_pairs > 0) {
+    // one sorted tile per thread (n_tiles <= kSplitPlanMaxTiles <= 1024)
+    const bool in = tid < n_tiles;
+    const int t = in ? (int)(keys[tid] & 0xffffffffu) : 0;
+    const int aux = in ? s_aux[t] : 0;
+    const int pages = aux >> 1;
+    const long long total = (long long)block_scan(pages, s_scan, tid).y * n_kv;
+    const int target = max(kMinChunkPages, (int)((total + n_cus - 1) / n_cus));
+    int S = 1;
+    if ((aux & 1) && 2 * pages > 3 * target) S = min(kMaxChunks, min(pages, (pages + target - 1) / target));
+    const int2 asked = block_scan(S - 1, s_scan, tid);   // exclusive prefix, total
+    if (asked.x + S - 1 > max_extra_pairs) S = 1;
+    const int2 extra = block_scan(S - 1, s_scan, tid);
+    const int2 slot = block_scan(S > 1 ? S : 0, s_scan, tid);
+    const int2 split = block_scan(S > 1 ? 1 : 0, s_scan, tid);
+    if (in)
+      for (int c = 0; c < S; ++c) pairs[tid + extra.x + c] = make_int4(t, c | (S << 8), slot.x, split.x);
+    if (tid == 0) *n_pairs = n_tiles + extra.y;
+    for (int i = tid; i < split.y * n_kv; i += 1024) tickets[i] = 0;
+  } else {
+    for (int i = tid; i < n_tiles; i += 1024) pairs[i] = make_int4((int)(keys[i] & 0xffffffffu), 1 << 8, 0, 0);
+    if (tid == 0) *n_pairs = n_tiles;
+  }
 }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
@@ -73,9 +191,54 @@ void paged_prefill_bf16_kernel(PrefillParams P) {
 
 int prefill_max_pages_per_row() { return kTabCache; }
 
-size_t prefill_workspace_bytes(int n_tokens, int /*n_kv_heads*/) {
-  const size_t tiles = (size_t)(n_tokens + kTile - 1) / kTile;
-  return (tiles * sizeof(int) + 255) / 256 * 256;
+namespace {
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of the bfloat16 prefill: [pair count][pairs][merge tickets][partial
+// states of split chunks]. Extra chunks: up to one spare workgroup per CU (as
+// pairs: CUs / KV heads), for plans of at most kSplitPlanMaxTiles tiles.
+struct PrefillLayout {
+  int n_tiles, max_extra_pairs;
+  size_t pairs, tickets, partials, total;
+};
+
+PrefillLayout prefill_layout(int n_tokens, int n_kv) {
+  PrefillLayout L;
+  L.n_tiles = (n_tokens + kTile - 1) / kTile;
+  const int cus = device_cus(), kv = std::max(n_kv, 1);
+  L.max_extra_pairs = L.n_tiles <= kSplitPlanMaxTiles
+                          ? std::min(std::max(1, cus / kv), L.n_tiles * (kMaxChunks - 1))
+                          : 0;
+  size_t off = 256;   // the pair count
+  L.pairs = off;
+  off += align256((size_t)(L.n_tiles + L.max_extra_pairs) * sizeof(int4));
+  L.tickets = off;
+  off += align256((size_t)L.max_extra_pairs * n_kv * sizeof(int));
+  L.partials = off;
+  // a split tile of S chunks adds S - 1 pairs and needs S <= 2 (S - 1) chunk states
+  off += (size_t)2 * L.max_extra_pairs * n_kv * kTile * kGroup * kPartialFloats * sizeof(float);
+  L.total = align256(off);
+  return L;
+}
+
+}  // namespace
+
+size_t prefill_workspace_bytes(int n_tokens, int n_kv_heads) {
+  return prefill_layout(n_tokens, n_kv_heads).total;
 }
 
 size_t segment_start_bytes(int n_tokens) { return ((size_t)n_tokens * sizeof(int) + 255) / 256 * 256; }
@@ -87,26 +250,37 @@ hipError_t launch_segment_start(hipStream_t stream, int n_tokens, const int32_t*
 }
 
 hipError_t launch_prefill_bf16(hipStream_t stream, const AttnArgs& a) {
-  const int n_tiles = (a.n_queries + kTile - 1) / kTile;
-  int* order = nullptr;
+  const PrefillLayout L = prefill_layout(a.n_queries, a.n_kv_heads);
+  char* ws = static_cast<char*>(a.workspace);
   int* lo = nullptr;
-  if (a.segments)   // packed form: first visible positions after the tile order
-    lo = reinterpret_cast<int*>(static_cast<char*>(a.workspace) + prefill_workspace_bytes(a.n_queries, a.n_kv_heads));
-  if (n_tiles <= kPlanMaxTiles) {
-    order = static_cast<int*>(a.workspace);
-    if (lo)
-      hipLaunchKernelGGL(packed_plan_kernel, dim3(1), dim3(1024), 0, stream, a.n_queries, a.positions,
-                         a.segments, lo, n_tiles, order);
-    else
-      hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, a.n_queries, a.positions,
-                         nullptr, n_tiles, order);
+  if (a.segments)   // packed form: first visible positions after the prefill workspace
+    lo = reinterpret_cast<int*>(ws + L.total);
+  PrefillParams P;
+  P.order = nullptr;
+  P.pairs = nullptr;
+  P.n_pairs = nullptr;
+  P.tickets = nullptr;
+  P.partials = nullptr;
+  P.partial_ml = nullptr;
+  int grid = L.n_tiles * a.n_kv_heads;
+  if (L.n_tiles <= kPlanMaxTiles) {
+    int* n_pairs = reinterpret_cast<int*>(ws);
+    int4* pairs = reinterpret_cast<int4*>(ws + L.pairs);
+    P.n_pairs = n_pairs;
+    P.pairs = pairs;
+    P.tickets = reinterpret_cast<int*>(ws + L.tickets);
+    P.partials = reinterpret_cast<float*>(ws + L.partials);
+    P.partial_ml = P.partials + (size_t)2 * L.max_extra_pairs * a.n_kv_heads * kTile * kGroup * kHeadDim;
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, a.n_queries, a.positions,
+                       a.segments, lo, a.rows, a.n_table_rows, a.pages_per_row * kPageSize, L.n_tiles,
+                       a.n_kv_heads, device_cus(), L.max_extra_pairs, n_pairs, pairs, P.tickets);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    grid = (L.n_tiles + L.max_extra_pairs) * a.n_kv_heads;
   } else if (lo) {
     hipError_t e = launch_segment_start(stream, a.n_queries, a.positions, a.segments, lo);
     if (e != hipSuccess) return e;
   }
-  PrefillParams P;
   P.n_tokens = a.n_queries;
   P.n_kv = a.n_kv_heads;
   P.q = (const uint16_t*)a.q;
@@ -120,10 +294,9 @@ hipError_t launch_prefill_bf16(hipStream_t stream, const AttnArgs& a) {
   P.positions = a.positions;
   P.scale_log2 = a.scale * kLog2e;
   P.out = a.out;
-  P.order = order;
   P.lo = lo;
   P.gate = (const uint16_t*)a.gate;
-  hipLaunchKernelGGL(paged_prefill_bf16_kernel, dim3(n_tiles * a.n_kv_heads), dim3(512), 0, stream, P);
+  hipLaunchKernelGGL(paged_prefill_bf16_kernel, dim3(grid), dim3(512), 0, stream, P);
   return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kTile = 64;
 constexpr int kPlanMaxTiles = 8192;
+constexpr int kMaxChunks = 8;          // key chunks of one split tile at most
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -112,10 +113,22 @@ struct PrefillParams {
   const int* positions;
   float scale_log2;
   float* out;
-  const int* order;
+  const int* order;   // tile order (used when pairs is null)
   const int* lo;   // first visible position per token (packed form), or null (0)
   const uint16_t* gate;   // optional output gate [n_tokens][n_q*128], bf16
+  // Key-split work list from the split plan (null: one item per tile and KV head):
+  // pair k = (tile, chunk s | chunks S << 8, first partial slot, split index);
+  // item = k * n_kv + g. A chunk of a split tile covers pages [s*len/S, (s+1)*len/S)
+  // of its run's len visible pages and leaves a partial state; the last chunk of
+  // (tile, g) to finish merges them.
+  const int4* pairs;
+  const int* n_pairs;
+  int* tickets;        // [split tiles][n_kv], zeroed by the plan
+  float* partials;     // O: [slot][n_kv][64 tokens][4 heads][128]
+  float* partial_ml;   // (m, l): [slot][n_kv][64 tokens][4 heads][2]
 };
+
+constexpr int kPartialFloats = kHeadDim + 2;   // m, l, O[128] of one (token, head)
 
 __device__ __forceinline__ bf16x8 join(i16x4 a, i16x4 b) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -218,12 +231,133 @@ __device__ __forceinline__ void page_barrier() {
 // Eight waves: wave w is query head 4g + (w & 3) for the 32 queries
 // 32*(w >> 2) .. +31 of the tile, two waves per SIMD. Pages are copied straight
 // from HBM into LDS (global_load_lds) one page ahead of the computation.
+// Partial state of one chunk of a split tile, then, in the last chunk of (tile, g)
+// to finish, the exact merge of all chunks' states into the output:
+//   M = max_s m_s,  out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// (m in the softmax's scaled log2 units; O and l relative to 2^m). The states are
+// written with plain vector stores; each wave drains them, the workgroup meets at
+// a barrier, and one agent-scope release precedes the ticket (per tile and KV
+// head); the last chunk takes one agent-scope acquire before reading them. No
+// workgroup waits for another.
+__device__ __forceinline__ void split_epilogue(const PrefillParams& P, const f32x16 (&o)[4], float m, float lt,
+                                               bool active, int qn, int hq, int lh, int g, int chunk, int n_chunks,
+                                               int slot0, int split, int t0, int tid) {
+  __shared__ int s_last;
+  const int n_q = P.n_kv * kGroup;
+  // opaque copies: the addresses below are formed here, not hoisted to the item's
+  // start, where they would stay live (and spill) through the page loop
+  asm volatile("" : "+v"(qn), "+v"(lh), "+v"(tid));
+  // (chunk s, token q, head h) -> row of 128 floats of O, 2 floats of (m, l)
+  auto row = [&](int s, int q, int h) -> int64_t {
+    return (((int64_t)(slot0 + s) * P.n_kv + g) * kTile + q) * kGroup + h;
+  };
+  if (active) {
+    const int64_t r = row(chunk, qn, hq);
+    float* op = P.partials + r * kHeadDim + 4 * lh;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(op + 32 * dt + 8 * j) =
+            f32x4{o[dt][4 * j], o[dt][4 * j + 1], o[dt][4 * j + 2], o[dt][4 * j + 3]};
+    if (lh == 0) *reinterpret_cast<float2*>(P.partial_ml + 2 * r) = make_float2(m, lt);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int old = __hip_atomic_fetch_add(&P.tickets[split * P.n_kv + g], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == n_chunks - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // weights 2^(m_s - M) / L per (token, head, chunk), in the free K page buffer
+  float* wts = reinterpret_cast<float*>(sK0);   // [64][4][kMaxChunks]
+  if (tid < kTile * kGroup) {
+    const int q = tid >> 2, h = tid & 3;
+    if (sRow[q] >= 0) {
+      float2 ml[kMaxChunks];
+#pragma unroll
+      for (int s = 0; s < kMaxChunks; ++s)
+        ml[s] = s < n_chunks ? *reinterpret_cast<const float2*>(P.partial_ml + 2 * row(s, q, h))
+                             : make_float2(-INFINITY, 0.f);
+      float M = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < kMaxChunks; ++s) M = fmaxf(M, ml[s].x);
+      float L = 0.f, f[kMaxChunks];
+#pragma unroll
+      for (int s = 0; s < kMaxChunks; ++s) {
+        f[s] = ml[s].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[s].x - M);
+        L += f[s] * ml[s].y;
+      }
+      const float inv = 1.0f / L;
+#pragma unroll
+      for (int s = 0; s < kMaxChunks; ++s) wts[(q * kGroup + h) * kMaxChunks + s] = f[s] * inv;
+    }
+  }
+  __syncthreads();
+  // rows (token, head) = 256, 32 per wave; a row is 128 floats, 2 per lane; 4 rows
+  // x every chunk loaded per batch
+  const int wv = tid >> 6, ln = tid & 63;
+  constexpr int kRows = 4;
+  for (int r0 = wv * 32; r0 < wv * 32 + 32; r0 += kRows) {
+    float2 x[kRows][kMaxChunks];
+#pragma unroll
+    for (int u = 0; u < kRows; ++u)
+#pragma unroll
+      for (int s = 0; s < kMaxChunks; ++s)
+        x[u][s] = s < n_chunks ? *reinterpret_cast<const float2*>(
+                                     P.partials + row(s, (r0 + u) >> 2, (r0 + u) & 3) * kHeadDim + 2 * ln)
+                               : make_float2(0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int q = (r0 + u) >> 2, h = (r0 + u) & 3;
+      if (sRow[q] < 0) continue;
+      float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int s = 0; s < kMaxChunks; ++s) {
+        const float wgt = wts[(q * kGroup + h) * kMaxChunks + s];   // 0 past n_chunks
+        acc.x += wgt * x[u][s].x;
+        acc.y += wgt * x[u][s].y;
+      }
+      const int64_t oi = ((int64_t)(t0 + q) * n_q + g * kGroup + h) * kHeadDim + 2 * ln;
+      if (P.gate) {   // output gate: out *= sigmoid(gate) at the same element
+        const uint32_t gw = *reinterpret_cast<const uint32_t*>(P.gate + oi);
+        acc.x *= sigmoidf(bf16_lo(gw));
+        acc.y *= sigmoidf(bf16_hi(gw));
+      }
+      *reinterpret_cast<float2*>(P.out + oi) = acc;
+    }
+  }
+  __syncthreads();   // the weights' LDS is the next item's page buffer
+}
+
 // One work item (64-token tile, KV head) by a workgroup of 512 threads; tid is the
 // thread's index in the workgroup.
+// kSplits: the item may be a chunk of a split tile (P.pairs from the split plan).
+template <bool kSplits = true>
 __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int item, const int tid) {
   const int n_q = P.n_kv * kGroup;
-  const int tile = P.order ? P.order[item / P.n_kv] : item / P.n_kv;
   const int g = item % P.n_kv;
+  int tile, chunk = 0, n_chunks = 1, slot0 = 0, split = 0;
+  if (kSplits && P.pairs) {
+    const int k = item / P.n_kv;
+    // both loads in one round trip: pairs has a slot for every workgroup of the grid
+    const int n_pairs = *P.n_pairs;
+    const int4 pr = P.pairs[k];
+    asm volatile("" : : "s"(n_pairs), "s"(pr.x), "s"(pr.y), "s"(pr.z), "s"(pr.w));   // not sunk past the test
+    if (k >= n_pairs) return;   // a spare workgroup: fewer chunks than the grid allows
+    tile = pr.x;
+    chunk = pr.y & 0xff;
+    n_chunks = pr.y >> 8;
+    slot0 = pr.z;
+    split = pr.w;
+  } else {
+    tile = P.order ? P.order[item / P.n_kv] : item / P.n_kv;
+  }
   const int w = tid >> 6;
   const int l = tid & 63;
   const int lq = l & 31;        // query index within the wave's 32 queries
@@ -306,11 +440,19 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
       mf = min(mf, __shfl_xor(mf, mm));
     }
     const int maxp = uniform(mp);
-    const int j0 = uniform(mf) / kPageSize;   // first page any query of the run sees
-    const int npages = maxp / kPageSize + 1;
+    // pages [j0, npages) of the run: from the first page any query of the run sees
+    // to the page of its last position; a chunk of a split tile takes its share
+    int j0 = uniform(mf) / kPageSize;
+    int npages = maxp / kPageSize + 1;
+    if (n_chunks > 1) {
+      const int len = npages - j0;
+      const int b = j0;
+      j0 = b + chunk * len / n_chunks;
+      npages = b + (chunk + 1) * len / n_chunks;
+    }
     const int* trow = P.table + (int64_t)r * P.pages_per_row;
     bool bad = false;
-    for (int i = tid; i < npages; i += 512) {
+    for (int i = j0 + tid; i < npages; i += 512) {
       const int id = trow[i];
       sTab[i] = id;
       bad |= id < 0 || id >= P.num_pages;
@@ -529,6 +671,10 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
 
     // ---- normalise and store: lane holds dims 32dt + 8j + 4lh + i of its query
     const float lt = lsum + __shfl_xor(lsum, 32);
+    if (kSplits && n_chunks > 1) {   // a chunk of a split tile: its one run is done; partial state, merge
+      split_epilogue(P, o, m, lt, active, qn, w & 3, lh, g, chunk, n_chunks, slot0, split, t0, tid);
+      return;
+    }
     if (active) {
       const int t = t0 + qn;
       const float inv = 1.0f / lt;

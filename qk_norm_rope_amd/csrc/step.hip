@@ -160,7 +160,7 @@ void step_paged_kernel(StepParams S) {
       int t = tid;
       asm volatile("" : "+v"(t));
       if (it < S.n_prefill_items) {
-        prefill_item(S.pre, it, t);
+        prefill_item<false>(S.pre, it, t);
       } else if (it - S.n_prefill_items < S.n_decode_items) {
         decode_slice<8>(S.dec, it - S.n_prefill_items, S.n_decode_items, s_prefix, t);
       } else {
@@ -259,6 +259,11 @@ hipError_t launch_step(hipStream_t stream, const StepArgs& a) {
   Pp.order = S.order;
   Pp.lo = nullptr;
   Pp.gate = nullptr;
+  Pp.pairs = nullptr;   // one item per tile and KV head, in plan order
+  Pp.n_pairs = nullptr;
+  Pp.tickets = nullptr;
+  Pp.partials = nullptr;
+  Pp.partial_ml = nullptr;
 
   const int grid = step_grid(R);
   DecodeParams& D = S.dec;
