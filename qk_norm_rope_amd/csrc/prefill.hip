@@ -69,6 +69,17 @@ __device__ int2 block_scan(int v, int* s_scan, int tid) {
   return make_int2(before + x - v, total);
 }
 
+// The same over the 64 lanes of one wave (no barriers).
+__device__ int2 wave_scan(int v, int lane) {
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return make_int2(x - v, __shfl(x, 63));
+}
+
 constexpr int kSplitPlanMaxTiles = 512;   // tiles for which the plan considers key splits
 constexpr int kMinChunkPages = 4;          // pages of a chunk at least (a chunk's set-up is ~2 pages)
 
@@ -83,11 +94,39 @@ constexpr int kMinChunkPages = 4;          // pages of a chunk at least (a chunk
 //     min(8, ceil(p / T)) chunks; in the sorted order, a tile gets its chunks if
 //     the extra chunks asked for up to and including it fit the grid's spare
 //     workgroups; the chunks take the tile's place in the order. Every step is
-//     a block-wide sum or scan, one tile per thread.
+//     a sum or scan, one tile per thread.
+// Up to 64 tiles, steps 3-5 run in one wave, one tile per lane: the sort is a
+// bitonic network over the lanes and the scans are shuffles, with no barrier.
 //     (A split costs a merge: partial states through memory, a release and an
 //     acquire that write back and invalidate the XCD's L2; below 1.5 T it loses.)
 //  5. the tickets of the split tiles' merges are zeroed.
 // Without splits the list is the sorted tiles, one pair each.
+// Steps 4-5 for the tile of sorted rank i (in: i < n_tiles) whose sorted key is
+// key; scan is block_scan or wave_scan over the threads taking part, stride their
+// count. Splits only when max_extra_pairs > 0.
+template <class Scan>
+__device__ void assign_pairs(int i, bool in, unsigned long long key, const int* s_aux, int n_tiles, int n_kv,
+                             int n_cus, int max_extra_pairs, int* n_pairs, int4* pairs, int* tickets, int stride,
+                             Scan scan) {
+  const int t = in ? (int)(key & 0xffffffffu) : 0;
+  const int aux = in ? s_aux[t] : 0;
+  const int pages = aux >> 1;
+  const long long total = (long long)scan(pages).y * n_kv;
+  const int target = max(kMinChunkPages, (int)((total + n_cus - 1) / n_cus));
+  int S = 1;
+  if (max_extra_pairs > 0 && (aux & 1) && 2 * pages > 3 * target)
+    S = min(kMaxChunks, min(pages, (pages + target - 1) / target));
+  const int2 asked = scan(S - 1);   // exclusive prefix, total
+  if (asked.x + S - 1 > max_extra_pairs) S = 1;
+  const int2 extra = scan(S - 1);
+  const int2 slot = scan(S > 1 ? S : 0);
+  const int2 split = scan(S > 1 ? 1 : 0);
+  if (in)
+    for (int c = 0; c < S; ++c) pairs[i + extra.x + c] = make_int4(t, c | (S << 8), slot.x, split.x);
+  if (i == 0) *n_pairs = n_tiles + extra.y;
+  for (int j = i; j < split.y * n_kv; j += stride) tickets[j] = 0;
+}
+
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(
     int n_tokens, const int* __restrict__ positions, const int* __restrict__ segments, int* __restrict__ lo,
     const int* __restrict__ rows, int n_table_rows, int max_pos, int n_tiles, int n_kv, int n_cus,
@@ -144,6 +183,23 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(
     }
   }
   __syncthreads();
+  if (n_tiles <= 64) {
+    if (wave != 0) return;
+    const bool in = lane < n_tiles;
+    unsigned long long key = in ? keys[lane] : ~0ull;
+    for (int k = 2; k <= 64; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        const unsigned klo = (unsigned)key, khi = (unsigned)(key >> 32);
+        const unsigned long long other =
+            ((unsigned long long)(unsigned)__shfl_xor((int)khi, j) << 32) | (unsigned)__shfl_xor((int)klo, j);
+        const bool keep_min = ((lane & j) == 0) == ((lane & k) == 0);
+        key = keep_min ? (other < key ? other : key) : (other > key ? other : key);
+      }
+    }
+    assign_pairs(lane, in, key, s_aux, n_tiles, n_kv, n_cus, n_tiles <= kSplitPlanMaxTiles ? max_extra_pairs : 0,
+                 n_pairs, pairs, tickets, 64, [&](int v) { return wave_scan(v, lane); });
+    return;
+  }
   for (int k = 2; k <= npow2; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = tid; i < npow2; i += 1024) {
@@ -157,25 +213,9 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(
       __syncthreads();
     }
   }
-  if (max_extra_pairs > 0) {
-    // one sorted tile per thread (n_tiles <= kSplitPlanMaxTiles <= 1024)
-    const bool in = tid < n_tiles;
-    const int t = in ? (int)(keys[tid] & 0xffffffffu) : 0;
-    const int aux = in ? s_aux[t] : 0;
-    const int pages = aux >> 1;
-    const long long total = (long long)block_scan(pages, s_scan, tid).y * n_kv;
-    const int target = max(kMinChunkPages, (int)((total + n_cus - 1) / n_cus));
-    int S = 1;
-    if ((aux & 1) && 2 * pages > 3 * target) S = min(kMaxChunks, min(pages, (pages + target - 1) / target));
-    const int2 asked = block_scan(S - 1, s_scan, tid);   // exclusive prefix, total
-    if (asked.x + S - 1 > max_extra_pairs) S = 1;
-    const int2 extra = block_scan(S - 1, s_scan, tid);
-    const int2 slot = block_scan(S > 1 ? S : 0, s_scan, tid);
-    const int2 split = block_scan(S > 1 ? 1 : 0, s_scan, tid);
-    if (in)
-      for (int c = 0; c < S; ++c) pairs[tid + extra.x + c] = make_int4(t, c | (S << 8), slot.x, split.x);
-    if (tid == 0) *n_pairs = n_tiles + extra.y;
-    for (int i = tid; i < split.y * n_kv; i += 1024) tickets[i] = 0;
+  if (max_extra_pairs > 0) {   // one sorted tile per thread (n_tiles <= kSplitPlanMaxTiles <= 1024)
+    assign_pairs(tid, tid < n_tiles, tid < n_tiles ? keys[tid] : 0ull, s_aux, n_tiles, n_kv, n_cus, max_extra_pairs,
+                 n_pairs, pairs, tickets, 1024, [&](int v) { return block_scan(v, s_scan, tid); });
   } else {
     for (int i = tid; i < n_tiles; i += 1024) pairs[i] = make_int4((int)(keys[i] & 0xffffffffu), 1 << 8, 0, 0);
     if (tid == 0) *n_pairs = n_tiles;
