@@ -206,6 +206,11 @@ __device__ __forceinline__ void decode_slice(const DecodeParams& P, const int gi
     const uint16_t* kbase = P.k_pool + (int64_t)g * pool_slots * kHeadDim;
     const uint16_t* vbase = P.v_pool + (int64_t)g * pool_slots * kHeadDim;
     const int* trow = P.table + (int64_t)b * P.pages_per_row;
+    // page ids of the segment's pages, 64 at a time: lane i holds the id of page
+    // win + i (loaded with q, so no page's K/V load waits on a table load); a
+    // wave moves its window when it reaches a page past it (pages rise)
+    int win = p0;
+    int tbl = p0 + l < pe ? trow[p0 + l] : -1;
 
     float m[kGroup], lsum[kGroup], acc[kGroup][8];
 #pragma unroll
@@ -217,7 +222,11 @@ __device__ __forceinline__ void decode_slice(const DecodeParams& P, const int gi
     }
 
     auto fetch = [&](int p, PageRegs& r) {
-      const int64_t page = trow[p];
+      if (p - win >= 64) {
+        win = p;
+        tbl = p + l < pe ? trow[p + l] : -1;
+      }
+      const int64_t page = __builtin_amdgcn_readlane(tbl, p - win);
       r.ok = page >= 0 && page < P.num_pages;
       const int64_t pg = r.ok ? page : 0;
       const uint16_t* krow = kbase + (pg * kPageSize + 16 * kw + hr) * kHeadDim + 8 * G4;
