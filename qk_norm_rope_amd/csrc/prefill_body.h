@@ -465,7 +465,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
     const int fill_row = uniform(last_ok ? maxp % kPageSize : 0);
     // some page of the run is outside the pool: only then does the softmax look pages up
     const bool any_bad = __syncthreads_or(bad);
-    auto page_of = [&](int p) -> int64_t { return p < npages ? sTab[p] : -1; };
+    // the LDS read is unconditional (clamped index), so its wait falls at the first
+    // use of the id instead of right after the read
+    auto page_of = [&](int p) -> int64_t {
+      const int v = sTab[min(max(p, j0), npages - 1)];
+      return (p >= j0 && p < npages) ? v : -1;
+    };
     auto page_ok = [&](int64_t page) { return page >= 0 && page < P.num_pages; };
 
     const bool active = qn >= a && qn < e;
