@@ -21,9 +21,9 @@
 //       row-major V page with ds_read_b64_tr_b16, P^T straight from the S^T
 //       accumulators (keys permuted the same way on both operands).
 // Pages reach three LDS buffers through 16-byte LDS-direct buffer loads with an
-// XOR-swizzled layout. Waves w and w + 4 share a SIMD and run half a page apart:
-// in each phase one issues the MFMAs of PV(j-1) and S(j) while the other runs the
-// softmax. A tile that holds tokens of several rows runs once per row ("run");
+// XOR-swizzled layout, issued by waves 4..7 in the phases where they run the
+// softmax. Waves w and w + 4 share a SIMD and run half a page apart: in each phase
+// one issues the MFMAs of PV(j-1) and S(j) while the other runs the softmax. A tile that holds tokens of several rows runs once per row ("run");
 // masking uses each token's position. A plan kernel orders tiles by decreasing
 // cost (largest visible position) so the long ones start first; item i maps to KV
 // head i % 8, which keeps one KV head's pages on one XCD's L2.
@@ -417,9 +417,11 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
     vofs[dt] = vrow * kRowBytes + (((4 * dt + 2 * ((l >> 4) & 1) + ((jj & 3) >> 1)) ^ v_swz(vrow)) << 4) + 8 * (jj & 1);
-  // page copy: instruction q of the wave fills rows 4(2w + q) .. +3; lane i takes
-  // row 4(2w + q) + i/16 and the global chunk that belongs at slot i % 16
-  const int crow0 = 8 * w + (l >> 4);
+  // page copy, by waves 4..7 only (they issue it in the phases where they run the
+  // softmax, so the MFMA stream of waves 0..3 carries no copy instructions):
+  // instruction q of wave w fills rows 16(w - 4) + 4q .. +3; lane i takes row
+  // 16(w - 4) + 4q + i/16 and the global chunk that belongs at slot i % 16
+  const int crow0 = 16 * (w - 4) + (l >> 4);
   const int cslot = l & 15;
 
   // lane l holds token l of the tile; runs are found with ballots and a wave max
@@ -494,8 +496,8 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
-    // copy page p into buffer B: wave w moves rows 8w..8w+7 of K and of V with two
-    // 1 KB instructions each. Rows past the run's last position, and pages past
+    // copy page p into buffer B: wave w >= 4 moves rows 16(w - 4)..+15 of K and of V
+    // with four 1 KB instructions each. Rows past the run's last position, and pages past
     // the run or outside the pool, copy the run's last valid row instead (finite
     // data; those keys are masked), so every step issues the same copies and the
     // compiler tracks which buffer each copy targets. The page is addressed
@@ -508,15 +510,17 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
       const int lim = ok ? maxp - p * kPageSize : -1;   // rows <= lim hold real keys
       const __amdgpu_buffer_rsrc_t rk = page_rsrc(kbase + src * kPageSize * kHeadDim);
       const __amdgpu_buffer_rsrc_t rv = page_rsrc(vbase + src * kPageSize * kHeadDim);
+      if (w >= 4) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int row = crow0 + 4 * q;
-        const int srow = row <= lim ? row : fill_row;
-        const int ko = srow * kRowBytes + ((cslot ^ k_swz(row)) << 4);
-        const int vo = srow * kRowBytes + ((cslot ^ v_swz(row)) << 4);
-        const int dst = (8 * uniform(w) + 4 * q) * kRowBytes;   // scalar LDS offset
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kbuf<B>() + dst), 16, ko, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vbuf<B>() + dst), 16, vo, 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+          const int row = crow0 + 4 * q;
+          const int srow = row <= lim ? row : fill_row;
+          const int ko = srow * kRowBytes + ((cslot ^ k_swz(row)) << 4);
+          const int vo = srow * kRowBytes + ((cslot ^ v_swz(row)) << 4);
+          const int dst = (16 * (uniform(w) - 4) + 4 * q) * kRowBytes;   // scalar LDS offset
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kbuf<B>() + dst), 16, ko, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vbuf<B>() + dst), 16, vo, 0, 0, 0);
+        }
       }
     };
 
