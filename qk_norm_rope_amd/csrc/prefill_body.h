@@ -367,6 +367,23 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
   const int t0 = tile * kTile;
   const int max_pos = P.pages_per_row * kPageSize;
 
+  // Q^T operand: lane holds query qn, dims 16*ks + 8*lh .. +7. Loaded first: the
+  // addresses depend only on the tile, so the loads overlap those of the tile's
+  // rows and positions instead of following them.
+  bf16x8 qb[8];
+  {
+    const int t = t0 + qn;
+    if (t < P.n_tokens) {
+      const uint16_t* qp = P.q + ((int64_t)t * n_q + head) * kHeadDim + 8 * lh;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qb[ks][i] = (__bf16)0.0f;
+    }
+  }
   if (tid < kTile) {
     const int t = t0 + tid;
     int r = -1, p = -1, f = 0;
@@ -382,23 +399,8 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
   }
   __syncthreads();
 
-  // Q^T operand: lane holds query qn, dims 16*ks + 8*lh .. +7
   const int qpos = sPos[qn];
   const int qlo = sLo[qn];   // first visible position of the lane's query
-  bf16x8 qb[8];
-  {
-    const int t = t0 + qn;
-    if (t < P.n_tokens) {
-      const uint16_t* qp = P.q + ((int64_t)t * n_q + head) * kHeadDim + 8 * lh;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qb[ks][i] = (__bf16)0.0f;
-    }
-  }
 
   const int64_t pool_slots = P.num_pages * kPageSize;
   const uint16_t* kbase = P.k_pool + (int64_t)g * pool_slots * kHeadDim;
@@ -667,13 +669,18 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
     fetch(Buf<0>{}, j0, page_of(j0));
     fetch(Buf<2>{}, npages, -1);   // finite rows for the zero-weight PV of the first phase
     next_page = page_of(j0 + 1);
-    for (int j = 0; j <= nrel; j += 3) {
+    // page steps j = 0 .. nrel (the last one only finishes PV(nrel - 1)); the
+    // buffer rotation is unrolled by three and left as soon as step nrel is done
+    for (int j = 0;; j += 3) {
       phase_even(Buf<0>{}, Buf<2>{}, Buf<1>{}, j);
       phase_odd(Buf<0>{}, Buf<2>{}, j);
+      if (j >= nrel) break;
       phase_even(Buf<1>{}, Buf<0>{}, Buf<2>{}, j + 1);
       phase_odd(Buf<1>{}, Buf<0>{}, j + 1);
+      if (j + 1 >= nrel) break;
       phase_even(Buf<2>{}, Buf<1>{}, Buf<0>{}, j + 2);
       phase_odd(Buf<2>{}, Buf<1>{}, j + 2);
+      if (j + 2 >= nrel) break;
     }
     wait_vmcnt<0>();
     __syncthreads();   // all reads of the page buffers and sTab are done before the next run
