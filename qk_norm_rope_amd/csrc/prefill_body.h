@@ -23,7 +23,8 @@
 // Pages reach three LDS buffers through 16-byte LDS-direct buffer loads with an
 // XOR-swizzled layout, issued by waves 4..7 in the phases where they run the
 // softmax. Waves w and w + 4 share a SIMD and run half a page apart: in each phase
-// one issues the MFMAs of PV(j-1) and S(j) while the other runs the softmax. A tile that holds tokens of several rows runs once per row ("run");
+// one issues the MFMAs of PV(j-1) and S(j) while the other runs the softmax. The
+// page loop is compiled once per group of four waves. A tile that holds tokens of several rows runs once per row ("run");
 // masking uses each token's position. A plan kernel orders tiles by decreasing
 // cost (largest visible position) so the long ones start first; item i maps to KV
 // head i % 8, which keeps one KV head's pages on one XCD's L2.
@@ -594,7 +595,6 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
     //   phase 2j  : group 0 PV(j-1) + S(j)   | group 1 softmax(j-1)
     //   phase 2j+1: group 0 softmax(j)       | group 1 PV(j-1) + S(j)
     // Page j+1 is copied in during phases 2j..2j+1 into the buffer page j-2 used.
-    const int grp = w >> 2;
     const int nrel = npages - j0;   // pages of the run from its first visible one
     int64_t next_page = 0;   // table entry of the page the next even phase copies
     // PV(j-1) then S(j) as one stream of 32 MFMAs whose LDS operands are read
@@ -648,40 +648,56 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
         pin(st[1]);
       }
     };
-    auto phase_even = [&](auto KBc, auto VBc, auto NBc, int j) {
-      wait_vmcnt<0>();        // page j's copies (issued two phases ago) are in LDS
-      page_barrier();
-      fetch(NBc, j0 + j + 1, next_page);
-      next_page = page_of(j0 + j + 2);   // read now, used by the next even phase
-      if (grp == 0) mfma_phase(KBc, VBc, j);
-      else if (j >= 1 && j - 1 < nrel) softmax(j0 + j - 1);
-    };
-    auto phase_odd = [&](auto KBc, auto VBc, int j) {
-      page_barrier();
-      if (grp == 0) { if (j < nrel) softmax(j0 + j); }
-      else mfma_phase(KBc, VBc, j);
-    };
-
+    // The page loop is compiled once per group (waves 0-3 and waves 4-7 take
+    // different branches of a wave-uniform test), so values one group keeps across
+    // a phase do not occupy registers in the other group's code. Both copies meet
+    // the same barriers in the same order.
+    auto page_loop = [&](auto Gc) {
+      constexpr int G = decltype(Gc)::value;
+      auto phase_even = [&](auto KBc, auto VBc, auto NBc, int j) {
+        wait_vmcnt<0>();        // page j's copies (issued two phases ago) are in LDS
+        page_barrier();
+        if constexpr (G == 1) {
+          fetch(NBc, j0 + j + 1, next_page);
+          next_page = page_of(j0 + j + 2);   // read now, used by the next even phase
+          if (j >= 1 && j - 1 < nrel) softmax(j0 + j - 1);
+        } else {
+          mfma_phase(KBc, VBc, j);
+        }
+      };
+      auto phase_odd = [&](auto KBc, auto VBc, int j) {
+        page_barrier();
+        if constexpr (G == 0) {
+          if (j < nrel) softmax(j0 + j);
+        } else {
+          mfma_phase(KBc, VBc, j);
+        }
+      };
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pb[c][i] = (__bf16)0.0f;
-    fetch(Buf<0>{}, j0, page_of(j0));
-    fetch(Buf<2>{}, npages, -1);   // finite rows for the zero-weight PV of the first phase
-    next_page = page_of(j0 + 1);
-    // page steps j = 0 .. nrel (the last one only finishes PV(nrel - 1)); the
-    // buffer rotation is unrolled by three and left as soon as step nrel is done
-    for (int j = 0;; j += 3) {
-      phase_even(Buf<0>{}, Buf<2>{}, Buf<1>{}, j);
-      phase_odd(Buf<0>{}, Buf<2>{}, j);
-      if (j >= nrel) break;
-      phase_even(Buf<1>{}, Buf<0>{}, Buf<2>{}, j + 1);
-      phase_odd(Buf<1>{}, Buf<0>{}, j + 1);
-      if (j + 1 >= nrel) break;
-      phase_even(Buf<2>{}, Buf<1>{}, Buf<0>{}, j + 2);
-      phase_odd(Buf<2>{}, Buf<1>{}, j + 2);
-      if (j + 2 >= nrel) break;
-    }
+        for (int i = 0; i < 8; ++i) pb[c][i] = (__bf16)0.0f;
+      if constexpr (G == 1) {
+        fetch(Buf<0>{}, j0, page_of(j0));
+        fetch(Buf<2>{}, npages, -1);   // finite rows for the zero-weight PV of the first phase
+        next_page = page_of(j0 + 1);
+      }
+      // page steps j = 0 .. nrel (the last one only finishes PV(nrel - 1)); the
+      // buffer rotation is unrolled by three and left as soon as step nrel is done
+      for (int j = 0;; j += 3) {
+        phase_even(Buf<0>{}, Buf<2>{}, Buf<1>{}, j);
+        phase_odd(Buf<0>{}, Buf<2>{}, j);
+        if (j >= nrel) break;
+        phase_even(Buf<1>{}, Buf<0>{}, Buf<2>{}, j + 1);
+        phase_odd(Buf<1>{}, Buf<0>{}, j + 1);
+        if (j + 1 >= nrel) break;
+        phase_even(Buf<2>{}, Buf<1>{}, Buf<0>{}, j + 2);
+        phase_odd(Buf<2>{}, Buf<1>{}, j + 2);
+        if (j + 2 >= nrel) break;
+      }
+    };
+    if (uniform(w) < 4) page_loop(Buf<0>{});
+    else page_loop(Buf<1>{});
     wait_vmcnt<0>();
     __syncthreads();   // all reads of the page buffers and sTab are done before the next run
 
