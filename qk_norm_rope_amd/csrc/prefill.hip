@@ -69,15 +69,17 @@ __device__ int2 block_scan(int v, int* s_scan, int tid) {
   return make_int2(before + x - v, total);
 }
 
-// The same over the 64 lanes of one wave (no barriers).
-__device__ int2 wave_scan(int v, int lane) {
+// The same over the 64 lanes of one wave, with DPP row shifts and row broadcasts
+// (no barriers, no LDS round trips).
+__device__ int2 wave_scan_dpp(int v) {
   int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  return make_int2(x - v, __shfl(x, 63));
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return make_int2(x - v, __builtin_amdgcn_readlane(x, 63));
 }
 
 constexpr int kSplitPlanMaxTiles = 512;   // tiles for which the plan considers key splits
@@ -95,14 +97,14 @@ constexpr int kMinChunkPages = 4;          // pages of a chunk at least (a chunk
 //     the extra chunks asked for up to and including it fit the grid's spare
 //     workgroups; the chunks take the tile's place in the order. Every step is
 //     a sum or scan, one tile per thread.
-// Up to 64 tiles, steps 3-5 run in one wave, one tile per lane: the sort is a
-// bitonic network over the lanes and the scans are shuffles, with no barrier.
+// Up to 64 tiles, steps 3-5 run in one wave, one tile per lane: a rank sort
+// through LDS (each lane counts the keys below its own) and DPP scans.
 //     (A split costs a merge: partial states through memory, a release and an
 //     acquire that write back and invalidate the XCD's L2; below 1.5 T it loses.)
 //  5. the tickets of the split tiles' merges are zeroed.
 // Without splits the list is the sorted tiles, one pair each.
 // Steps 4-5 for the tile of sorted rank i (in: i < n_tiles) whose sorted key is
-// key; scan is block_scan or wave_scan over the threads taking part, stride their
+// key; scan is block_scan or wave_scan_dpp over the threads taking part, stride their
 // count. Splits only when max_extra_pairs > 0.
 template <class Scan>
 __device__ void assign_pairs(int i, bool in, unsigned long long key, const int* s_aux, int n_tiles, int n_kv,
@@ -187,17 +189,20 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(
     if (wave != 0) return;
     const bool in = lane < n_tiles;
     unsigned long long key = in ? keys[lane] : ~0ull;
-    for (int k = 2; k <= 64; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        const unsigned klo = (unsigned)key, khi = (unsigned)(key >> 32);
-        const unsigned long long other =
-            ((unsigned long long)(unsigned)__shfl_xor((int)khi, j) << 32) | (unsigned)__shfl_xor((int)klo, j);
-        const bool keep_min = ((lane & j) == 0) == ((lane & k) == 0);
-        key = keep_min ? (other < key ? other : key) : (other > key ? other : key);
-      }
+    {
+      // rank sort: keys are distinct (the tile index is in the low word); each lane
+      // counts the keys below its own and places it there
+      int rank = 0;
+      for (int k = 0; k < n_tiles; ++k) rank += keys[k] < key ? 1 : 0;
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      if (in) keys[64 + rank] = key;   // keys holds kPlanMaxTiles >= 128 entries
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      key = in ? keys[64 + lane] : ~0ull;
     }
     assign_pairs(lane, in, key, s_aux, n_tiles, n_kv, n_cus, n_tiles <= kSplitPlanMaxTiles ? max_extra_pairs : 0,
-                 n_pairs, pairs, tickets, 64, [&](int v) { return wave_scan(v, lane); });
+                 n_pairs, pairs, tickets, 64, [&](int v) { return wave_scan_dpp(v); });
     return;
   }
   for (int k = 2; k <= npow2; k <<= 1) {
