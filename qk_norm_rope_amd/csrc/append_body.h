@@ -52,16 +52,27 @@ template <> struct Vec8<uint16_t> {
   }
 };
 
-// Pairwise float32 sum of n values, neighbours first, an odd last one carried up
-// a level (the order the whole-vector norm pins). v (in LDS) is overwritten.
-__device__ __forceinline__ float pair_sums(float* v, int n) {
-  while (n > 1) {
-    const int m = n & ~1;
-    for (int i = 0; i < m; i += 2) v[i >> 1] = v[i] + v[i + 1];
-    if (n & 1) v[m >> 1] = v[m];
-    n = (n + 1) >> 1;
+// Pairwise float32 sum of the n <= 256 non-negative values v[0..n), neighbours
+// first, an odd last one carried up a level (the order the whole-vector norm
+// pins), by one wave; the result is in lane 0. The values are padded with zeros
+// to a power of two: adding +0 leaves a non-negative partial sum unchanged, so the
+// balanced tree over the padded values adds exactly what the carried-up order
+// adds. Lane l holds the padded values [l*per, (l+1)*per) and adds them pairwise
+// in-lane (the first levels); xor shuffles do the rest.
+__device__ __forceinline__ float pair_sums_wave(const float* v, int n, int lane) {
+  int np2 = 1;
+  while (np2 < n) np2 <<= 1;
+  const int per = np2 > 64 ? np2 / 64 : 1;   // 1, 2 or 4
+  const int lanes = np2 / per;
+  float x[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = lane * per + u;
+    x[u] = (u < per && i < n) ? v[i] : 0.f;
   }
-  return v[0];
+  float t = per == 4 ? (x[0] + x[1]) + (x[2] + x[3]) : (per == 2 ? x[0] + x[1] : x[0]);
+  for (int m = 1; m < lanes; m <<= 1) t = t + __shfl_xor(t, m);
+  return t;
 }
 
 constexpr int kMaxWholeHeads = 256;   // q heads + kv heads for the whole-vector norm
@@ -113,6 +124,18 @@ __device__ __forceinline__ void append_token(
   }
   const float* cs_row = rope_cos + (int64_t)pos * half_r;
   const float* sn_row = rope_sin + (int64_t)pos * half_r;
+  // partial rotary: cos/sin of the lane's first-half elements 8j + i, read once per
+  // token (element e < R/2 uses entry e, R/2 <= e < R entry e - R/2)
+  float pc[8], pz[8];
+  if (PARTIAL) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = 8 * j + i;
+      const int idx = e < half_r ? e : e - half_r;
+      pc[i] = e < rotary_dim ? cs_row[idx] : 0.f;
+      pz[i] = e < rotary_dim ? sn_row[idx] : 0.f;
+    }
+  }
 
   const int n_norm = n_q_heads + n_kv_heads;
   auto source = [&](int hv) -> const TIn* {
@@ -145,11 +168,14 @@ __device__ __forceinline__ void append_token(
       }
     }
     __syncthreads();
-    if (tid < 2) {   // thread 0: the q heads' sums, thread 1: the k heads'
-      const int nh = tid == 0 ? n_q_heads : n_kv_heads;
-      const float total = pair_sums(s_ss[tid], nh);
-      const float ms = total / (float)(nh * kHeadDim);
-      s_r[tid] = 1.0f / __builtin_sqrtf(ms + eps);
+    if (tid < 128) {   // wave 0: the q heads' sums, wave 1: the k heads'
+      const int which = tid >> 6;
+      const int nh = which == 0 ? n_q_heads : n_kv_heads;
+      const float total = pair_sums_wave(s_ss[which], nh, tid & 63);
+      if ((tid & 63) == 0) {
+        const float ms = total / (float)(nh * kHeadDim);
+        s_r[which] = 1.0f / __builtin_sqrtf(ms + eps);
+      }
     }
     __syncthreads();
   }
@@ -213,24 +239,27 @@ __device__ __forceinline__ void append_token(
         yrow[kHeadDim / 2 + 8 * j + i] = yb[i];
       }
       __builtin_amdgcn_wave_barrier();
-      auto rot = [&](int e, float y) -> float {
+      // cv, sv: cos and sin of the element's rotation angle
+      auto rot = [&](int e, float y, float cv, float sv) -> float {
         if (e < half_r) {
-          const float ye = y * cs_row[e];
-          const float ps = yrow[e + half_r] * sn_row[e];
+          const float ye = y * cv;
+          const float ps = yrow[e + half_r] * sv;
           return ye - ps;
         }
         if (e < rotary_dim) {
-          const int i = e - half_r;
-          const float ye = y * cs_row[i];
-          const float ps = yrow[i] * sn_row[i];
+          const float ye = y * cv;
+          const float ps = yrow[e - half_r] * sv;
           return ye + ps;
         }
         return y;
       };
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        oa[i] = rot(8 * j + i, ya[i]);
-        ob[i] = rot(kHeadDim / 2 + 8 * j + i, yb[i]);
+        oa[i] = rot(8 * j + i, ya[i], pc[i], pz[i]);
+        // second-half elements rotate only when R > 64 (entry e - R/2)
+        const int e = kHeadDim / 2 + 8 * j + i;
+        const bool r2 = e < rotary_dim;
+        ob[i] = rot(e, yb[i], r2 ? cs_row[e - half_r] : 0.f, r2 ? sn_row[e - half_r] : 0.f);
       }
       __builtin_amdgcn_wave_barrier();   // the row is rewritten by the group's next head
     }
