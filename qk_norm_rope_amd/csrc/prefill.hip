@@ -196,7 +196,8 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(
       for (int k = 0; k < n_tiles; ++k) rank += keys[k] < key ? 1 : 0;
       __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_wave_barrier();
-      if (in) keys[64 + rank] = key;   // keys holds kPlanMaxTiles >= 128 entries
+      static_assert(kPlanMaxTiles >= 128, "the ranked keys go to keys[64..127]");
+      if (in) keys[64 + rank] = key;
       __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_wave_barrier();
       key = in ? keys[64 + lane] : ~0ull;

@@ -24,10 +24,11 @@
 // XOR-swizzled layout, issued by waves 4..7 in the phases where they run the
 // softmax. Waves w and w + 4 share a SIMD and run half a page apart: in each phase
 // one issues the MFMAs of PV(j-1) and S(j) while the other runs the softmax. The
-// page loop is compiled once per group of four waves. A tile that holds tokens of several rows runs once per row ("run");
-// masking uses each token's position. A plan kernel orders tiles by decreasing
-// cost (largest visible position) so the long ones start first; item i maps to KV
-// head i % 8, which keeps one KV head's pages on one XCD's L2.
+// page loop is compiled once per group of four waves. A tile that holds tokens of
+// several rows runs once per row ("run"); masking uses each token's position. A
+// plan kernel orders tiles by decreasing cost (largest visible position) so the
+// long ones start first; item i maps to KV head i % 8, which keeps one KV head's
+// pages on one XCD's L2.
 #pragma once
 #include "common.h"
 
