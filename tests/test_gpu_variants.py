@@ -99,3 +99,37 @@ def test_output_gate_decode_prefill_packed(dtype):
     ref = O.packed(q_out[:P], w.dtype, k_rows[:P], v_rows[:P], w.dtype, w.rows, w.positions, W.SCALE)
     torch.cuda.synchronize()
     assert max_abs_err(pre.cpu().numpy(), O.output_gate(ref, gate_host[:P], w.dtype)) <= tol
+
+
+@pytest.mark.parametrize("kv,rotary", [(3, 0), (5, 64), (17, 0), (40, 32)])
+def test_whole_norm_append_head_counts(kv, rotary):
+    # head counts that are not powers of two (the head sums are added pairwise with
+    # an odd one carried up) and above 64 (several sums per lane in the reduction)
+    Q = lib()
+    w = W.build(f"variants_kv{kv}", 60 + kv, "bf16", num_pages=16, pages_per_row=8, n_table_rows=3,
+                chunks=[(0, 0, 40), (1, 9, 30)], decode=[(2, 77)], decode_row0=2, n_kv_heads=kv)
+    R = rotary or W.HEAD_DIM
+    nq, nk = w.n_q_heads, w.n_kv_heads
+    print(f"whole-norm append: {nq} query heads, {nk} KV heads, rotary_dim={R}", flush=True)
+    rng = np.random.default_rng(61 + kv)
+    gq = rng.uniform(0.5, 1.5, nq * W.HEAD_DIM).astype(np.float32)
+    gk = rng.uniform(0.5, 1.5, nk * W.HEAD_DIM).astype(np.float32)
+    cos, sin = Q.rope_table(O.ROPE_THETA, 512, R)
+    run = Run(w, keep_pre=False)
+    t = run.t
+    q_out = torch.empty((w.n_tokens, nq * W.HEAD_DIM), dtype=run.td, device=DEV)
+    Q.qknorm_rope_append(t["q"], t["k"], t["v"], torch.from_numpy(gq).to(DEV), torch.from_numpy(gk).to(DEV),
+                         torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV), run.positions_all(),
+                         q_out, run.k_pool, run.v_pool, slots=t["slots"], table=t["decode_table"],
+                         qk_norm_whole=True, rotary_dim=rotary)
+    torch.cuda.synchronize()
+    every_at = np.concatenate([w.positions, w.step_positions]).astype(np.int64)
+    oq, ok_, ov = O.append(w.q, w.k, w.v, w.dtype, w.dtype, gq, gk, every_at, n_q_heads=nq, n_kv_heads=nk,
+                           norm_whole=True, rotary_dim=R)
+    assert np.array_equal(host_values(q_out, w.dtype), oq)
+    _, _, _, every_slot = oracle_append(w)
+    sl = torch.from_numpy(every_slot).to(DEV)
+    kp = host_values(run.k_pool[:, sl].permute(1, 0, 2).contiguous(), w.dtype)
+    vp = host_values(run.v_pool[:, sl].permute(1, 0, 2).contiguous(), w.dtype)
+    assert np.array_equal(kp, ok_)
+    assert np.array_equal(vp, ov)
