@@ -26,7 +26,8 @@
 //   * online softmax per head, row max by DPP rotations inside 16-lane rows;
 //   * P.V on the vector ALU, lane l holding 8 dimensions of 4 keys, the
 //     probabilities passed through LDS;
-//   * the next page's K/V loads are in flight while the current page computes.
+//   * the next page's K/V loads (non-temporal: each byte is read once) are in
+//     flight while the current page computes.
 // Partial states travel through agent-coherent (sc1) stores and loads with an
 // explicit wait before the ticket, so no cache-wide write-back is needed.
 #pragma once
@@ -232,10 +233,14 @@ __device__ __forceinline__ void decode_slice(const DecodeParams& P, const int gi
       const uint16_t* krow = kbase + (pg * kPageSize + 16 * kw + hr) * kHeadDim + 8 * G4;
       const uint16_t* vrow = vbase + (pg * kPageSize + 16 * kw + 4 * G4) * kHeadDim + 8 * hr;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) r.k[st] = *reinterpret_cast<const bf16x8*>(krow + 32 * st);
+      for (int st = 0; st < 4; ++st) {
+        // K and V rows are read once per call: streaming (non-temporal) loads
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + 32 * st));
+        r.k[st] = __builtin_bit_cast(bf16x8, x);
+      }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        // V rows are read whole and once: streaming (non-temporal) loads
+        // each V row is read whole, once
         const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vrow + jj * kHeadDim));
         r.v[jj] = make_uint4(x[0], x[1], x[2], x[3]);
       }
