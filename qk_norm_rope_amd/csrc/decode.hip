@@ -63,12 +63,15 @@ hipError_t launch_decode_bf16(hipStream_t stream, const AttnArgs& a) {
   P.partials = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + counter_bytes);
   // Large batches take two workgroups per resident slot: slices halve and the
   // workgroups that finish first take the rest, which evens out the slices'
-  // different segment counts (64 ragged rows: 277 us instead of 290; 128 rows:
-  // unchanged). Small batches keep one (their time is a chain of memory round
-  // trips, which a second round of workgroups only lengthens). The host knows only
-  // the bound rows x KV heads x pages per row on the units.
+  // different segment counts (64 ragged rows: 5.4 TB/s instead of 5.1). Smaller
+  // ones keep one: each workgroup pays a fixed set-up and merge, which a second
+  // round of workgroups with half the units each only repeats (128 rows at 1 KV
+  // head: 5.2 TB/s with one round, 4.4 with two; 8 rows: a chain of memory round
+  // trips that a second round lengthens). The host knows only the bound
+  // rows x KV heads x pages per row on the units; two rounds from 300 units per
+  // resident workgroup.
   int grid = grid_for_device();
-  if ((int64_t)a.n_queries * a.n_kv_heads * a.pages_per_row >= 32LL * grid) grid = std::min(kMaxGrid, 2 * grid);
+  if ((int64_t)a.n_queries * a.n_kv_heads * a.pages_per_row >= 300LL * grid) grid = std::min(kMaxGrid, 2 * grid);
   const size_t lds = (size_t)(a.n_queries + 1) * sizeof(int);
   hipLaunchKernelGGL(paged_decode_bf16_kernel, dim3(grid), dim3(256), lds, stream, P);
   return hipGetLastError();
