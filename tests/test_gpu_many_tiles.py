@@ -3,12 +3,14 @@ Entries table, prefill_paged: prompts packed end to end, each token attending ov
 its row's pages up to its position).
 
 Up to 64 tiles of 64 tokens, one wave sorts the tiles by cost and assigns key
-splits; above that the whole planning workgroup sorts and scans, and above 512
-tiles the plan orders tiles without splitting any. These cases run those paths at
-8 KV heads and, where splits are planned, at 1 KV head (one GPU's share of heads
-sharded 8 ways). The pool bytes are checked bit for bit; attention outputs within
-the bfloat16 tolerance on sampled tokens that include every prompt's first and
-last token, so the longest tiles (the first ones in the plan's order) are covered.
+splits; above that the whole planning workgroup sorts and scans, above 512 tiles
+the plan orders tiles without splitting any, and above 8192 tiles there is no plan
+(tiles run in pack order). These cases run those paths at 8 KV heads and at 1 KV
+head (one GPU's share of heads sharded 8 ways). The pool bytes are checked bit for
+bit; attention outputs within the bfloat16 tolerance on sampled tokens that include
+the first and last token of every prompt (of the first and last few prompts when
+there are many), so the longest tiles (the first ones in the plan's order) are
+covered.
 """
 import numpy as np
 import pytest
@@ -36,7 +38,7 @@ def _need_gpu():
     torch.cuda.empty_cache()
 
 
-def _check(w, chunks, seed, n_random):
+def _check(w, chunks, seed, n_random, max_ends=None):
     run = Run(w)
     run.step()
     ref_q, k_rows, v_rows, slots = oracle_append(w)
@@ -48,6 +50,8 @@ def _check(w, chunks, seed, n_random):
     for _, _, n in chunks:
         ends += [start, start + n - 1]
         start += n
+    if max_ends is not None and len(ends) > max_ends:
+        ends = ends[:max_ends // 2] + ends[-(max_ends // 2):]
     rng = np.random.default_rng(seed)
     toks = sorted(set(ends + [int(x) for x in rng.choice(P, n_random, replace=False)]))
     ref = O.prefill(ref_q[:P], w.dtype, kp, vp, w.dtype, w.table, w.rows, w.positions, W.SCALE, tokens=toks,
@@ -71,3 +75,12 @@ def test_prefill_with_516_tiles():
                 chunks=CHUNKS_516)
     print(f"[many tiles] P={w.n_prefill}, 8 KV heads", flush=True)
     _check(w, CHUNKS_516, 181, 40)
+
+
+def test_prefill_with_8200_tiles_without_a_plan():
+    # 128 prompts of 4100 tokens (524800 tokens, 8200 tiles) at 1 KV head
+    chunks = [(r, 0, 4100) for r in range(128)]
+    w = W.build("many_tiles_8200", 91, "bf16", num_pages=8400, pages_per_row=65, n_table_rows=128,
+                chunks=chunks, n_kv_heads=1)
+    print(f"[many tiles] P={w.n_prefill}, 1 KV head", flush=True)
+    _check(w, chunks, 191, 40, max_ends=16)
