@@ -98,6 +98,16 @@ __device__ __forceinline__ int owner(long long u, long long U, int G) {
 }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// One (row, KV head) segment of a workgroup's slice: pages p0..pe-1 of row b's
+// pos / 64 + 1 pages for KV head g; whole when the slice holds all of them.
+struct DecodeSeg {
+  int b, pos, g, p0, pe, win, tbl;
+  long long seg_begin, seg_end, stop;
+  bool whole;
+  bf16x8 qa[4];
+};
+
 struct PageRegs {
   bf16x8 k[4];
   uint4 v[4];
@@ -176,44 +186,44 @@ __device__ __forceinline__ void decode_slice(const DecodeParams& P, const int gi
     b = lo;
   }
 
-  long long u = u0;
-  bool first_segment = true;
-  while (u < u1) {
-    while (s_prefix[b + 1] <= u) ++b;   // skip rows without units
-    const int pos = P.positions[b];
-    const int np = pos / kPageSize + 1;
-    const long long base = s_prefix[b];
-    const int g = (int)((u - base) / np);
-    const int p0 = (int)((u - base) % np);
-    const long long seg_begin = base + (long long)g * np;
-    const long long seg_end = seg_begin + np;
-    const long long stop = min(u1, seg_end);
-    const int pe = p0 + (int)(stop - u);
-    const bool whole = (p0 == 0) && (pe == np);
-
+  // Open the segment holding unit u (row cursor bb moves forward to its row): its
+  // page range in this slice, and the loads of its query operand and of the ids of
+  // its first 64 pages are issued.
+  auto open = [&](long long u, int& bb, DecodeSeg& sg) {
+    while (s_prefix[bb + 1] <= u) ++bb;   // skip rows without units
+    sg.b = bb;
+    sg.pos = P.positions[bb];
+    const int np = sg.pos / kPageSize + 1;
+    const long long base = s_prefix[bb];
+    sg.g = (int)((u - base) / np);
+    sg.p0 = (int)((u - base) % np);
+    sg.seg_begin = base + (long long)sg.g * np;
+    sg.seg_end = sg.seg_begin + np;
+    sg.stop = min(u1, sg.seg_end);
+    sg.pe = sg.p0 + (int)(sg.stop - u);
+    sg.whole = (sg.p0 == 0) && (sg.pe == np);
     // query operand: rows 0..3 = heads 4g..4g+3; k-slot 8*G4+i of step st = dim 8*(4*st+G4)+i,
     // so each K load of a step reads 64 contiguous bytes of every row
-    bf16x8 qa[4];
     if (hr < kGroup) {
-      const uint16_t* qp = P.q + ((int64_t)b * n_q + g * kGroup + hr) * kHeadDim;
+      const uint16_t* qp = P.q + ((int64_t)bb * n_q + sg.g * kGroup + hr) * kHeadDim;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const bf16x8*>(qp + 8 * (4 * st + G4));
+      for (int st = 0; st < 4; ++st) sg.qa[st] = *reinterpret_cast<const bf16x8*>(qp + 8 * (4 * st + G4));
     } else {
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qa[st][i] = (__bf16)0.0f;
+        for (int i = 0; i < 8; ++i) sg.qa[st][i] = (__bf16)0.0f;
     }
-    const uint16_t* kbase = P.k_pool + (int64_t)g * pool_slots * kHeadDim;
-    const uint16_t* vbase = P.v_pool + (int64_t)g * pool_slots * kHeadDim;
-    const int* trow = P.table + (int64_t)b * P.pages_per_row;
     // page ids of the segment's pages, 64 at a time: lane i holds the id of page
     // win + i (loaded with q, so no page's K/V load waits on a table load); a
     // wave moves its window when it reaches a page past it (pages rise)
-    int win = p0;
-    int tbl = p0 + l < pe ? trow[p0 + l] : -1;
+    const int* trow = P.table + (int64_t)bb * P.pages_per_row;
+    sg.win = sg.p0;
+    sg.tbl = sg.p0 + l < sg.pe ? trow[sg.p0 + l] : -1;
+  };
 
-    float m[kGroup], lsum[kGroup], acc[kGroup][8];
+  float m[kGroup], lsum[kGroup], acc[kGroup][8];
+  auto reset = [&]() {
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
       m[i] = -INFINITY;
@@ -221,98 +231,92 @@ __device__ __forceinline__ void decode_slice(const DecodeParams& P, const int gi
 #pragma unroll
       for (int d = 0; d < 8; ++d) acc[i][d] = 0.f;
     }
+  };
 
-    auto fetch = [&](int p, PageRegs& r) {
-      if (p - win >= 64) {
-        win = p;
-        tbl = p + l < pe ? trow[p + l] : -1;
-      }
-      const int64_t page = __builtin_amdgcn_readlane(tbl, p - win);
-      r.ok = page >= 0 && page < P.num_pages;
-      const int64_t pg = r.ok ? page : 0;
-      const uint16_t* krow = kbase + (pg * kPageSize + 16 * kw + hr) * kHeadDim + 8 * G4;
-      const uint16_t* vrow = vbase + (pg * kPageSize + 16 * kw + 4 * G4) * kHeadDim + 8 * hr;
+  auto fetch = [&](DecodeSeg& sg, int p, PageRegs& r) {
+    if (p - sg.win >= 64) {
+      const int* trow = P.table + (int64_t)sg.b * P.pages_per_row;
+      sg.win = p;
+      sg.tbl = p + l < sg.pe ? trow[p + l] : -1;
+    }
+    const int64_t page = __builtin_amdgcn_readlane(sg.tbl, p - sg.win);
+    r.ok = page >= 0 && page < P.num_pages;
+    const int64_t pg = r.ok ? page : 0;
+    const uint16_t* kbase = P.k_pool + (int64_t)sg.g * pool_slots * kHeadDim;
+    const uint16_t* vbase = P.v_pool + (int64_t)sg.g * pool_slots * kHeadDim;
+    const uint16_t* krow = kbase + (pg * kPageSize + 16 * kw + hr) * kHeadDim + 8 * G4;
+    const uint16_t* vrow = vbase + (pg * kPageSize + 16 * kw + 4 * G4) * kHeadDim + 8 * hr;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        // K and V rows are read once per call: streaming (non-temporal) loads
-        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + 32 * st));
-        r.k[st] = __builtin_bit_cast(bf16x8, x);
-      }
+    for (int st = 0; st < 4; ++st) {
+      // K and V rows are read once per call: streaming (non-temporal) loads
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + 32 * st));
+      r.k[st] = __builtin_bit_cast(bf16x8, x);
+    }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        // each V row is read whole, once
-        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vrow + jj * kHeadDim));
-        r.v[jj] = make_uint4(x[0], x[1], x[2], x[3]);
-      }
-    };
+    for (int jj = 0; jj < 4; ++jj) {
+      // each V row is read whole, once
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vrow + jj * kHeadDim));
+      r.v[jj] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
+  };
 
-    auto compute = [&](int p, const PageRegs& r) {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+auto compute = [&](const DecodeSeg& sg, int p, const PageRegs& r) {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < 4; ++st) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], r.k[st], sc, 0, 0, 0);
-      // lanes 0..15: sc[i] = score of head i with key p*64 + 16w + lane
-      const int key0 = p * kPageSize + 16 * kw;
-      const bool kvalid = r.ok && key0 + hr <= pos;
-      float pr[kGroup];
-      bool any_change = false;
-      float corr[kGroup];
+    for (int st = 0; st < 4; ++st) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sg.qa[st], r.k[st], sc, 0, 0, 0);
+    // lanes 0..15: sc[i] = score of head i with key p*64 + 16w + lane
+    const int key0 = p * kPageSize + 16 * kw;
+    const bool kvalid = r.ok && key0 + hr <= sg.pos;
+    float pr[kGroup];
+    bool any_change = false;
+    float corr[kGroup];
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        const float x = kvalid ? sc[i] * P.scale_log2 : -INFINITY;
-        const float pm = lane0(row_max16(x));
-        const float mn = fmaxf(m[i], pm);
-        corr[i] = (m[i] == mn) ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);
-        any_change |= (m[i] != mn);
-        const float ms = (mn == -INFINITY) ? 0.f : mn;
-        pr[i] = __builtin_amdgcn_exp2f(x - ms);
-        lsum[i] = lsum[i] * corr[i] + pr[i];
-        m[i] = mn;
-      }
-      if (l < 16) *reinterpret_cast<float4*>(&s_p[w][l][0]) = make_float4(pr[0], pr[1], pr[2], pr[3]);
-      __builtin_amdgcn_wave_barrier();
-      if (any_change) {
+    for (int i = 0; i < kGroup; ++i) {
+      const float x = kvalid ? sc[i] * P.scale_log2 : -INFINITY;
+      const float pm = lane0(row_max16(x));
+      const float mn = fmaxf(m[i], pm);
+      corr[i] = (m[i] == mn) ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);
+      any_change |= (m[i] != mn);
+      const float ms = (mn == -INFINITY) ? 0.f : mn;
+      pr[i] = __builtin_amdgcn_exp2f(x - ms);
+      lsum[i] = lsum[i] * corr[i] + pr[i];
+      m[i] = mn;
+    }
+    if (l < 16) *reinterpret_cast<float4*>(&s_p[w][l][0]) = make_float4(pr[0], pr[1], pr[2], pr[3]);
+    __builtin_amdgcn_wave_barrier();
+    if (any_change) {
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i)
+      for (int i = 0; i < kGroup; ++i)
 #pragma unroll
-          for (int d = 0; d < 8; ++d) acc[i][d] *= corr[i];
-      }
+        for (int d = 0; d < 8; ++d) acc[i][d] *= corr[i];
+    }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int kk = 4 * G4 + jj;
-        const bool vok = r.ok && key0 + kk <= pos;
-        const float4 ph = *reinterpret_cast<const float4*>(&s_p[w][kk][0]);
-        float vf[8];
-        vf[0] = bf16_lo(r.v[jj].x); vf[1] = bf16_hi(r.v[jj].x);
-        vf[2] = bf16_lo(r.v[jj].y); vf[3] = bf16_hi(r.v[jj].y);
-        vf[4] = bf16_lo(r.v[jj].z); vf[5] = bf16_hi(r.v[jj].z);
-        vf[6] = bf16_lo(r.v[jj].w); vf[7] = bf16_hi(r.v[jj].w);
+    for (int jj = 0; jj < 4; ++jj) {
+      const int kk = 4 * G4 + jj;
+      const bool vok = r.ok && key0 + kk <= sg.pos;
+      const float4 ph = *reinterpret_cast<const float4*>(&s_p[w][kk][0]);
+      float vf[8];
+      vf[0] = bf16_lo(r.v[jj].x); vf[1] = bf16_hi(r.v[jj].x);
+      vf[2] = bf16_lo(r.v[jj].y); vf[3] = bf16_hi(r.v[jj].y);
+      vf[4] = bf16_lo(r.v[jj].z); vf[5] = bf16_hi(r.v[jj].z);
+      vf[6] = bf16_lo(r.v[jj].w); vf[7] = bf16_hi(r.v[jj].w);
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          const float x = vok ? vf[d] : 0.f;
-          acc[0][d] += ph.x * x;
-          acc[1][d] += ph.y * x;
-          acc[2][d] += ph.z * x;
-          acc[3][d] += ph.w * x;
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-    };
-
-    {
-      constexpr int S = kStride;
-      const int q0 = NW == 4 ? p0 : p0 + (w >> 2);   // p0 < pe
-      PageRegs ra, rb;
-      if (NW == 4 || q0 < pe) fetch(q0, ra);
-      for (int p = q0; p < pe; p += 2 * S) {
-        if (p + S < pe) fetch(p + S, rb);
-        compute(p, ra);
-        if (p + 2 * S < pe) fetch(p + 2 * S, ra);
-        if (p + S < pe) compute(p + S, rb);
+      for (int d = 0; d < 8; ++d) {
+        const float x = vok ? vf[d] : 0.f;
+        acc[0][d] += ph.x * x;
+        acc[1][d] += ph.y * x;
+        acc[2][d] += ph.z * x;
+        acc[3][d] += ph.w * x;
       }
     }
+    __builtin_amdgcn_wave_barrier();
+  };
 
-    // ---- merge the wave's lanes (DPP rotations within 16 lanes, permlane swaps
-    // across the 16-lane groups: no LDS round trips), then the NW waves
+  auto finish = [&](const DecodeSeg& sg, bool first) {
+    // Finish a segment: merge the wave's lanes (DPP rotations within 16 lanes,
+    // permlane swaps across the 16-lane groups: no LDS round trips), then the NW
+    // waves; store the output, or the partial state and, in the last workgroup of
+    // a cut segment, merge the partials
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
       lsum[i] = row_sum16(lsum[i]);
@@ -348,13 +352,13 @@ __device__ __forceinline__ void decode_slice(const DecodeParams& P, const int gi
 #pragma unroll
       for (int c = 0; c < DPT; ++c) A[c] += f * s_acc[ww][hi][dd + c];
     }
-    float* orow = P.out + ((int64_t)b * n_q + g * kGroup + hi) * kHeadDim + dd;
+    float* orow = P.out + ((int64_t)sg.b * n_q + sg.g * kGroup + hi) * kHeadDim + dd;
     // output gate: out *= sigmoid(gate) at the same element
     float gt[DPT];
 #pragma unroll
     for (int c = 0; c < DPT; ++c) gt[c] = 1.f;
     if (P.gate) {
-      const uint16_t* gp = P.gate + ((int64_t)b * n_q + g * kGroup + hi) * kHeadDim + dd;
+      const uint16_t* gp = P.gate + ((int64_t)sg.b * n_q + sg.g * kGroup + hi) * kHeadDim + dd;
       if constexpr (DPT == 2) {
         const uint32_t gw = *reinterpret_cast<const uint32_t*>(gp);
         gt[0] = sigmoidf(bf16_lo(gw));
@@ -364,20 +368,20 @@ __device__ __forceinline__ void decode_slice(const DecodeParams& P, const int gi
         for (int c = 0; c < DPT; ++c) gt[c] = sigmoidf(bf16_lo(gp[c]));
       }
     }
-    if (whole) {
+    if (sg.whole) {
 #pragma unroll
       for (int c = 0; c < DPT; ++c) orow[c] = (A[c] / L) * gt[c];
     } else {
-      const int slot = first_segment ? 0 : 1;
+      const int slot = first ? 0 : 1;
       float* part = P.partials + ((int64_t)gi * 2 + slot) * kPartial + hi * (kHeadDim + 2);
       if ((tid % TPH) == 0) { store_sc1(part, M); store_sc1(part + 1, L); }
 #pragma unroll
       for (int c = 0; c < DPT; ++c) store_sc1(part + 2 + dd + c, A[c]);
       __builtin_amdgcn_s_waitcnt(0);   // the partial is at the coherence point before the ticket
       __syncthreads();
-      const int rg = b * P.n_kv + g;
-      const int i0 = owner(seg_begin, U, Gd);
-      const int i1 = owner(seg_end - 1, U, Gd);
+      const int rg = sg.b * P.n_kv + sg.g;
+      const int i0 = owner(sg.seg_begin, U, Gd);
+      const int i1 = owner(sg.seg_end - 1, U, Gd);
       // workgroups with an empty range (fewer units than workgroups) add no partial
       int count = 0;
       for (int i = i0; i <= i1; ++i) count += range_begin(i, U, Gd) < range_begin(i + 1, U, Gd);
@@ -388,7 +392,7 @@ __device__ __forceinline__ void decode_slice(const DecodeParams& P, const int gi
       __syncthreads();
       if (s_last) {
         // one pass over the partials in workgroup order, 8 partials' loads in flight at a time
-        const bool i0_first = range_begin(i0, U, Gd) >= seg_begin;
+        const bool i0_first = range_begin(i0, U, Gd) >= sg.seg_begin;
         float Mx = -INFINITY, Lt = 0.f, B[DPT];
 #pragma unroll
         for (int c = 0; c < DPT; ++c) B[c] = 0.f;
@@ -423,8 +427,60 @@ __device__ __forceinline__ void decode_slice(const DecodeParams& P, const int gi
       }
     }
     __syncthreads();   // LDS reuse by the next segment
-    first_segment = false;
-    u = stop;
+  };
+
+  int bb = b;
+  if constexpr (NW == 4) {
+    // One stream of pages over the slice's segments: while a segment runs, the
+    // next one is already open (row, q, page ids loaded), and its first page is
+    // fetched into the free buffer during the current segment's last page, so a
+    // segment boundary restarts no memory round trip.
+    DecodeSeg cur, nxt;
+    open(u0, bb, cur);
+    bool more = cur.stop < u1;
+    if (more) open(cur.stop, bb, nxt);
+    PageRegs ra, rb;
+    fetch(cur, cur.p0, ra);
+    bool first = true;
+    while (true) {
+      reset();
+      for (int p = cur.p0; p < cur.pe; p += 2) {
+        if (p + 1 < cur.pe) fetch(cur, p + 1, rb);
+        else if (more) fetch(nxt, nxt.p0, rb);
+        compute(cur, p, ra);
+        if (p + 2 < cur.pe) fetch(cur, p + 2, ra);
+        else if (p + 2 == cur.pe && more) fetch(nxt, nxt.p0, ra);
+        if (p + 1 < cur.pe) compute(cur, p + 1, rb);
+      }
+      finish(cur, first);
+      if (!more) break;
+      if ((cur.pe - cur.p0) & 1) ra = rb;   // the next segment's first page
+      cur = nxt;
+      first = false;
+      more = cur.stop < u1;
+      if (more) open(cur.stop, bb, nxt);
+    }
+  } else {
+    // wave w takes pages p0 + w / 4, p0 + w / 4 + 2, ... of each segment
+    long long u = u0;
+    bool first = true;
+    while (u < u1) {
+      DecodeSeg cur;
+      open(u, bb, cur);
+      reset();
+      const int q0 = cur.p0 + (w >> 2);
+      PageRegs ra, rb;
+      if (q0 < cur.pe) fetch(cur, q0, ra);
+      for (int p = q0; p < cur.pe; p += 2 * kStride) {
+        if (p + kStride < cur.pe) fetch(cur, p + kStride, rb);
+        compute(cur, p, ra);
+        if (p + 2 * kStride < cur.pe) fetch(cur, p + 2 * kStride, ra);
+        if (p + kStride < cur.pe) compute(cur, p + kStride, rb);
+      }
+      finish(cur, first);
+      first = false;
+      u = cur.stop;
+    }
   }
 }
 
