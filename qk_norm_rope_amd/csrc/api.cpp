@@ -333,7 +333,7 @@ int step_paged(void* stream, const qkr_pool* pool, int32_t n_prefill, int32_t n_
   if (!workspace || workspace_bytes < need) return QKR_EWORKSPACE;
   if (!qknr::step_enabled()) {
     snprintf(g_last_error, sizeof(g_last_error),
-             "step_paged: the single-launch kernel is switched off in this build; "
+             "step_paged: the single-launch kernel is switched off in this version of the library; "
              "call qknorm_rope_append, paged_prefill_attn and paged_decode_attn");
     return QKR_EUNSUPPORTED;
   }
