@@ -253,3 +253,24 @@ def test_decode_with_fewer_pages_than_workgroups(positions):
     kp, vp = oracle_pools(w, k_rows, v_rows, slots)
     ref = O.decode(ref_q, w.dtype, kp, vp, w.dtype, w.decode_table, w.step_positions, W.SCALE)
     assert max_abs_err(run.dec_out.cpu().numpy(), ref) <= TOL_BF16
+
+
+def test_decode_many_short_segments_per_workgroup():
+    # 1024 rows of 1-5 pages: each workgroup's slice holds many (row, KV head)
+    # segments of odd and even page counts, so every segment's first page is
+    # fetched during the previous segment's last page; every output is checked
+    rng = np.random.default_rng(47)
+    n = 1024
+    pos = rng.integers(0, 320, size=n)
+    pos[:6] = [0, 63, 64, 127, 128, 319]
+    w = W.build("many_segments", 47, "bf16", num_pages=n * 5 + 8, pages_per_row=5, n_table_rows=n,
+                decode=[(b, int(p)) for b, p in enumerate(pos)])
+    print(f"[parity] {n} decode rows of 1-5 pages", flush=True)
+    run = Run(w, keep_pre=False)
+    run.step()
+    ref_q, k_rows, v_rows, slots = oracle_append(w)
+    kp, vp = oracle_pools(w, k_rows, v_rows, slots)
+    ref = O.decode(ref_q, w.dtype, kp, vp, w.dtype, w.decode_table, w.step_positions, W.SCALE)
+    err = max_abs_err(run.dec_out.cpu().numpy(), ref)
+    print(f"[parity] many short segments max abs err {err:.3e}", flush=True)
+    assert err <= TOL_BF16
