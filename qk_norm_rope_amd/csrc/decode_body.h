@@ -27,7 +27,7 @@
 //   * P.V on the vector ALU, lane l holding 8 dimensions of 4 keys, the
 //     probabilities passed through LDS;
 //   * the next page's K/V loads (non-temporal: each byte is read once) are in
-//     flight while the current page computes.
+//     flight while the current page computes, across segment boundaries too.
 // Partial states travel through agent-coherent (sc1) stores and loads with an
 // explicit wait before the ticket, so no cache-wide write-back is needed.
 #pragma once
@@ -454,7 +454,7 @@ auto compute = [&](const DecodeSeg& sg, int p, const PageRegs& r) {
       }
       finish(cur, first);
       if (!more) break;
-      if ((cur.pe - cur.p0) & 1) ra = rb;   // the next segment's first page
+      if ((cur.pe - cur.p0) & 1) ra = rb;   // an odd page count left the next first page in rb
       cur = nxt;
       first = false;
       more = cur.stop < u1;
