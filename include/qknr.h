@@ -15,7 +15,8 @@
  *   Every call only enqueues work on that stream; nothing synchronises, nothing
  *   allocates device memory, and the library keeps no state between calls, so
  *   calls are thread-safe. Ordering (append before attention) comes from the
- *   stream.
+ *   stream. The one exception is paged_decode_attn_noalloc, which works in a
+ *   library-owned scratch array per GPU (see there).
  * - Ownership: the caller owns every buffer. Device pointers must stay valid
  *   until the enqueued work has finished.
  * - Activations are token-major: q is [n][num_q_heads*head_dim] and k, v are
@@ -199,6 +200,36 @@ int paged_decode_attn_ex(void* stream, const qkr_pool* pool, int32_t n_rows,
                          const int32_t* table, int32_t pages_per_row,
                          const int32_t* positions, float scale, float* out,
                          void* workspace, size_t workspace_bytes, const qkr_attn_opts* opts);
+
+/*
+ * paged_decode_attn_noalloc -- paged_decode_attn with no workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. It computes exactly what
+ * paged_decode_attn computes (the same kernel and the same split, so the same
+ * bits) and calls no allocating routine.
+ *
+ * Scratch: instead of a caller's workspace, the call uses a library-owned device
+ * array of QKR_NOALLOC_SCRATCH_BYTES (8.5 MiB) per GPU, held from the first call on
+ * that GPU until the process ends (its address is looked up once per device, on
+ * the first call with that device current). Each call clears the merge counters it
+ * uses with a small fill kernel on `stream`, then launches the decode kernel.
+ * Every call on one GPU shares that GPU's array and the array keeps the last
+ * call's contents, so calls that may overlap on one GPU (different streams,
+ * different threads without ordering) race and give wrong results: order them on
+ * one stream.
+ *
+ * Limit: n_rows * num_kv_heads <= QKR_NOALLOC_MAX_ROW_HEADS (12288 rows at 8 KV
+ * heads) for a bfloat16 pool, besides paged_decode_attn's own 12288 rows; larger
+ * batches return QKR_EUNSUPPORTED before anything is enqueued (qkr_last_error
+ * names the scratch limit). A float32 pool needs no
+ * scratch. The other arguments, errors and layouts are those of paged_decode_attn.
+ */
+#define QKR_NOALLOC_MAX_ROW_HEADS 98304
+#define QKR_NOALLOC_SCRATCH_BYTES (98304 * 4 + 2048 * 2 * 520 * 4)
+int paged_decode_attn_noalloc(void* stream, const qkr_pool* pool, int32_t n_rows,
+                              const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* table, int32_t pages_per_row,
+                              const int32_t* positions, float scale, float* out);
 
 /*
  * paged_prefill_attn -- packed prompt tokens over their rows' pages

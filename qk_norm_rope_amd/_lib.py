@@ -17,6 +17,7 @@ QKR_F32 = 0
 QKR_BF16 = 1
 HEAD_DIM = 128
 PAGE_SIZE = 64
+NOALLOC_MAX_ROW_HEADS = 98304   # QKR_NOALLOC_MAX_ROW_HEADS: rows x KV heads of paged_decode_attn_noalloc
 
 EXPORTED = (
     "qknorm_rope_append",
@@ -24,6 +25,7 @@ EXPORTED = (
     "paged_decode_attn",
     "paged_decode_attn_ex",
     "paged_decode_attn_workspace",
+    "paged_decode_attn_noalloc",
     "paged_prefill_attn",
     "paged_prefill_attn_ex",
     "paged_prefill_attn_workspace",
@@ -68,7 +70,7 @@ class AttnOpts(ctypes.Structure):
 
 class QknrError(RuntimeError):
     def __init__(self, status: int, where: str):
-        detail = LIB.qkr_last_error().decode() if status == -4 else ""
+        detail = LIB.qkr_last_error().decode() if status in (-2, -4) else ""
         super().__init__(f"{where}: {status_str(status)} ({status}){': ' + detail if detail else ''}")
         self.status = status
 
@@ -102,6 +104,8 @@ def _load():
                                        vp, vp, i32, vp, i32, vp, vp, vp]
     lib.paged_decode_attn.restype = ctypes.c_int
     lib.paged_decode_attn.argtypes = [vp, pool_p, i32, vp, vp, vp, vp, i32, vp, f32, vp, vp, sz]
+    lib.paged_decode_attn_noalloc.restype = ctypes.c_int
+    lib.paged_decode_attn_noalloc.argtypes = [vp, pool_p, i32, vp, vp, vp, vp, i32, vp, f32, vp]
     lib.paged_decode_attn_workspace.restype = sz
     lib.paged_decode_attn_workspace.argtypes = [pool_p, i32, i32]
     lib.paged_prefill_attn.restype = ctypes.c_int
@@ -260,6 +264,22 @@ def paged_decode_attn(q, k_pool, v_pool, table, positions, scale: float, out, wo
         float(scale), _ptr(out, "out", torch.float32, n_rows * n_q * HEAD_DIM),
         _ptr(workspace, "workspace"), ws_bytes, ctypes.byref(opts))
     _check(st, "paged_decode_attn")
+
+
+def paged_decode_attn_noalloc(q, k_pool, v_pool, table, positions, scale: float, out, stream=None) -> None:
+    """paged_decode_attn on the library's own per-GPU scratch: no workspace, no
+    allocation; calls that overlap on one GPU race (order them on one stream)."""
+    import torch
+    n_q = q.shape[-1] // HEAD_DIM
+    pool = pool_desc(k_pool, n_q)
+    n_rows = int(positions.numel())
+    ppr = int(table.shape[-1])
+    st = LIB.paged_decode_attn_noalloc(
+        _stream(stream), ctypes.byref(pool), n_rows, _ptr(q, "q", k_pool.dtype, n_rows * n_q * HEAD_DIM),
+        _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype),
+        _ptr(table, "table", torch.int32, n_rows * ppr), ppr, _ptr(positions, "positions", torch.int32),
+        float(scale), _ptr(out, "out", torch.float32, n_rows * n_q * HEAD_DIM))
+    _check(st, "paged_decode_attn_noalloc")
 
 
 def paged_prefill_attn(q, k_pool, v_pool, table, rows, positions, scale: float, out, workspace=None,

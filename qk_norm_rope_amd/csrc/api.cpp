@@ -241,6 +241,41 @@ int paged_decode_attn(void* stream, const qkr_pool* pool, int32_t n_rows,
                               positions, scale, out, workspace, workspace_bytes, nullptr);
 }
 
+int paged_decode_attn_noalloc(void* stream, const qkr_pool* pool, int32_t n_rows,
+                              const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* table, int32_t pages_per_row,
+                              const int32_t* positions, float scale, float* out) {
+  int st = check_pool(pool);
+  if (st != QKR_OK) return st;
+  if (n_rows < 0) return QKR_EINVAL;
+  if (n_rows == 0) return QKR_OK;
+  if (!q || !k_pool || !v_pool || !table || !positions || !out || pages_per_row <= 0) return QKR_EINVAL;
+  if (!std::isfinite(scale)) return QKR_EINVAL;
+  const bool bf16 = pool->dtype == QKR_BF16;
+  if (bf16 && n_rows > qknr::decode_max_rows()) return QKR_EUNSUPPORTED;
+  if (bf16 && (int64_t)n_rows * pool->num_kv_heads > qknr::decode_noalloc_max_pairs()) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "paged_decode_attn_noalloc: %d rows x %d KV heads exceed the scratch limit of %d (row, KV head) "
+             "pairs; use paged_decode_attn with a workspace",
+             (int)n_rows, (int)pool->num_kv_heads, qknr::decode_noalloc_max_pairs());
+    return QKR_EUNSUPPORTED;
+  }
+  qknr::AttnArgs a;
+  a.n_queries = n_rows;
+  a.n_q_heads = pool->num_q_heads;
+  a.n_kv_heads = pool->num_kv_heads;
+  a.bf16 = bf16;
+  a.q = q; a.k_pool = k_pool; a.v_pool = v_pool;
+  a.num_pages = pool->num_pages;
+  a.table = table; a.n_table_rows = n_rows; a.pages_per_row = pages_per_row;
+  a.rows = nullptr; a.positions = positions; a.scale = scale; a.out = out;
+  a.workspace = nullptr; a.workspace_bytes = 0;
+  a.gate = nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!bf16) return launch_status(qknr::launch_attention_generic(s, a));   // needs no scratch
+  return launch_status(qknr::launch_decode_bf16_noalloc(s, a));
+}
+
 size_t paged_prefill_attn_workspace(const qkr_pool* pool, int32_t n_tokens) {
   if (check_pool(pool) != QKR_OK || n_tokens <= 0) return 0;
   if (pool->dtype != QKR_BF16) return 0;

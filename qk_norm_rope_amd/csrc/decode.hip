@@ -2,9 +2,11 @@
 // each streaming an equal slice of the (row, KV head, page) units. The device
 // code (and its design) is in decode_body.h.
 #include <algorithm>
+#include <mutex>
 
 #include "decode_body.h"
 #include "kernels.h"
+#include "qknr.h"
 
 namespace qknr {
 namespace {
@@ -33,7 +35,68 @@ int grid_for_device() {
   return cached[dev];
 }
 
+// Scratch of the allocation-free entry point: the merge counters of at most
+// kNoAllocMaxPairs (row, KV head) segments, then the partial states of kMaxGrid
+// workgroups, laid out as launch_decode_bf16 expects a workspace. Each GPU the
+// library runs on holds one copy until the process ends; every call on that GPU
+// shares it.
+constexpr size_t kNoAllocCounterBytes = (size_t)kNoAllocMaxPairs * sizeof(int);
+constexpr size_t kNoAllocScratchBytes = kNoAllocCounterBytes + (size_t)kMaxGrid * 2 * kPartial * sizeof(float);
+static_assert(kNoAllocCounterBytes % 256 == 0, "partials start on a 256-byte boundary");
+static_assert(kNoAllocMaxPairs == QKR_NOALLOC_MAX_ROW_HEADS, "limit stated in the header");
+static_assert(kNoAllocScratchBytes == QKR_NOALLOC_SCRATCH_BYTES, "size stated in the header");
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on each device, looked up once per device with that
+// device current. In host code the array's name is only a stand-in for the symbol,
+// never a device address: kernels and copies take this pointer.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// The merge counters must start at zero: a fill kernel (not a memset node, so the
+// call can sit inside a captured graph) clears the ones a call uses.
+__global__ __launch_bounds__(256) void zero_ints_kernel(int* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 }  // namespace
+
+int decode_noalloc_max_pairs() { return kNoAllocMaxPairs; }
+
+hipError_t launch_decode_bf16_noalloc(hipStream_t stream, const AttnArgs& a) {
+  const int pairs = a.n_queries * a.n_kv_heads;   // <= kNoAllocMaxPairs, checked by the caller
+  if (pairs <= 0 || pairs > kNoAllocMaxPairs) return hipErrorInvalidValue;
+  void* ptr = nullptr;
+  hipError_t e = scratch_of_current_device(&ptr);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3((pairs + 255) / 256), dim3(256), 0, stream, static_cast<int*>(ptr),
+                     pairs);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  AttnArgs b = a;
+  b.workspace = ptr;
+  b.workspace_bytes = kNoAllocScratchBytes;
+  return launch_decode_bf16(stream, b);
+}
 
 size_t decode_workspace_bytes(int n_rows, int n_kv_heads, int /*pages_per_row*/) {
   const size_t pairs = (size_t)n_rows * n_kv_heads;

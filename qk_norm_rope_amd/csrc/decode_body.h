@@ -39,6 +39,7 @@ namespace {
 constexpr int kPartial = kGroup * (kHeadDim + 2);  // floats per partial: per head (m, l, acc[128])
 constexpr int kMaxGrid = 2048;                     // workgroups launched at most
 constexpr int kMaxRows = 12288;                    // rows per call (LDS prefix table)
+constexpr int kNoAllocMaxPairs = kMaxRows * 8;     // rows x KV heads of the allocation-free call
 
 struct DecodeParams {
   int n_rows, n_kv;

@@ -228,3 +228,33 @@ def test_size_limits_host_checks():
     pneed = lib.paged_prefill_attn_workspace(ctypes.byref(pool), 100)
     assert lib.paged_prefill_attn(None, ctypes.byref(pool), 100, FAKE, FAKE, FAKE, FAKE, 3, 2049, FAKE,
                                   FAKE, 0.1, FAKE, FAKE, pneed) == -2   # longer page table than prefill takes
+
+
+def test_noalloc_decode_host_checks():
+    # the allocation-free decode takes no workspace; its checks run before any
+    # device call, including the limit of its library-owned scratch
+    pool = _pool()
+    lib = L.LIB
+    assert lib.paged_decode_attn_noalloc(None, ctypes.byref(pool), 0, None, None, None, None, 0, None,
+                                         0.1, None) == 0
+    assert lib.paged_decode_attn_noalloc(None, ctypes.byref(pool), -1, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+                                         0.1, FAKE) == -1
+    assert lib.paged_decode_attn_noalloc(None, ctypes.byref(pool), 2, FAKE, FAKE, FAKE, None, 4, FAKE,
+                                         0.1, FAKE) == -1
+    assert lib.paged_decode_attn_noalloc(None, ctypes.byref(pool), 2, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+                                         float("nan"), FAKE) == -1
+    assert lib.paged_decode_attn_noalloc(None, ctypes.byref(_pool(head_dim=64)), 2, FAKE, FAKE, FAKE, FAKE,
+                                         4, FAKE, 0.1, FAKE) == -2
+    # 8 KV heads: the scratch holds exactly the kernel's 12288 rows
+    rows = L.NOALLOC_MAX_ROW_HEADS // 8 + 1
+    assert lib.paged_decode_attn_noalloc(None, ctypes.byref(pool), rows, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+                                         0.1, FAKE) == -2
+    # 16 KV heads: half the rows reach the scratch limit
+    p16 = _pool(num_q_heads=64, num_kv_heads=16)
+    assert lib.paged_decode_attn_noalloc(None, ctypes.byref(p16), L.NOALLOC_MAX_ROW_HEADS // 16 + 1, FAKE,
+                                         FAKE, FAKE, FAKE, 4, FAKE, 0.1, FAKE) == -2
+    assert "scratch" in L.last_error()
+    # fewer KV heads: the kernel's own row limit still holds
+    p4 = _pool(num_q_heads=16, num_kv_heads=4)
+    assert lib.paged_decode_attn_noalloc(None, ctypes.byref(p4), 12289, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+                                         0.1, FAKE) == -2
