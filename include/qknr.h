@@ -37,9 +37,10 @@
  *   an argument is invalid; QKR_ELAUNCH when the runtime refuses a launch.
  *   Device-side data (page ids, positions, slots, rows) is not validated
  *   against the caller's intent, but every index the kernels form is range
- *   checked: an out-of-range page id, position, row or slot makes that token's
- *   or row's output unspecified (it is skipped or reads nothing), never an
- *   out-of-bounds access.
+ *   checked, so bad data never causes an out-of-bounds access: a query whose
+ *   position or row is out of range gets NaN outputs; a page id outside the pool
+ *   makes the keys of that page invisible (the output is then unspecified but
+ *   finite); an out-of-range slot skips the write.
  * - The kernels are built for head_dim 128 and page_size 64; other values
  *   return QKR_EUNSUPPORTED.
  */

@@ -170,6 +170,14 @@ __device__ __forceinline__ void decode_slice(const DecodeParams& P, const int gi
     __syncthreads();
   }
   const long long U = s_prefix[n_rows];
+  // a row without units (position outside its table) gets NaN outputs, as the
+  // float32 kernel gives it: row b is written by slice b % Gd
+  for (int bb = gi; bb < n_rows; bb += Gd) {
+    if (s_prefix[bb + 1] == s_prefix[bb]) {
+      float* orow = P.out + (int64_t)bb * n_q * kHeadDim;
+      for (int e = tid; e < n_q * kHeadDim; e += NT) orow[e] = __builtin_nanf("");
+    }
+  }
   const long long u0 = range_begin(gi, U, Gd);
   const long long u1 = range_begin(gi + 1, U, Gd);
   if (u0 >= u1) return;

@@ -437,7 +437,18 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
     const int r = __builtin_amdgcn_readlane(my_row, a);
     const unsigned long long other = __ballot(l > a && my_row != r);
     const int e = other ? (int)__builtin_ctzll(other) : kTile;
-    if (r < 0) { a = e; continue; }
+    if (r < 0) {
+      // tokens with a row or position out of range: NaN outputs, as the float32
+      // kernel gives them (the tile's tail past the pack is left alone)
+      if (qn >= a && qn < e && t0 + qn < P.n_tokens) {
+        float* op = P.out + ((int64_t)(t0 + qn) * n_q + head) * kHeadDim + 64 * lh;
+        const float nan = __builtin_nanf("");
+#pragma unroll
+        for (int i = 0; i < 64; i += 4) *reinterpret_cast<f32x4*>(op + i) = f32x4{nan, nan, nan, nan};
+      }
+      a = e;
+      continue;
+    }
     int mp = (l >= a && l < e) ? my_pos : 0;
     int mf = (l >= a && l < e) ? my_lo : 0x7fffffff;
 #pragma unroll
@@ -446,9 +457,10 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
       mf = min(mf, __shfl_xor(mf, mm));
     }
     const int maxp = uniform(mp);
+    const int runlo = uniform(mf);   // smallest first visible position of the run
     // pages [j0, npages) of the run: from the first page any query of the run sees
     // to the page of its last position; a chunk of a split tile takes its share
-    int j0 = uniform(mf) / kPageSize;
+    int j0 = runlo / kPageSize;
     int npages = maxp / kPageSize + 1;
     if (n_chunks > 1) {
       const int len = npages - j0;
@@ -501,9 +513,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
       for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
     // copy page p into buffer B: wave w >= 4 moves rows 16(w - 4)..+15 of K and of V
-    // with four 1 KB instructions each. Rows past the run's last position, and pages past
-    // the run or outside the pool, copy the run's last valid row instead (finite
-    // data; those keys are masked), so every step issues the same copies and the
+    // with four 1 KB instructions each. Rows past the run's last position, and
+    // pages past the run or outside the pool, copy the run's last valid row instead;
+    // rows before the run's first visible position (history a packed prompt does
+    // not see, which need not be finite: a NaN V row would turn its zero weight
+    // into NaN) copy the first visible row of the same page. Both hold finite data
+    // and those keys are masked, so every step issues the same copies and the
     // compiler tracks which buffer each copy targets. The page is addressed
     // through a buffer descriptor (reads past the page return zero).
     auto fetch = [&](auto Bc, int p, int64_t page) {
@@ -512,13 +527,14 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
       const bool ok = page_ok(page);
       const int64_t src = ok ? page : fill_page;
       const int lim = ok ? maxp - p * kPageSize : -1;   // rows <= lim hold real keys
+      const int low = runlo - p * kPageSize;             // rows >= low are visible to the run (low <= lim)
       const __amdgpu_buffer_rsrc_t rk = page_rsrc(kbase + src * kPageSize * kHeadDim);
       const __amdgpu_buffer_rsrc_t rv = page_rsrc(vbase + src * kPageSize * kHeadDim);
       if (w >= 4) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = crow0 + 4 * q;
-          const int srow = row <= lim ? row : fill_row;
+          const int srow = row > lim ? fill_row : (row < low ? low : row);
           const int ko = srow * kRowBytes + ((cslot ^ k_swz(row)) << 4);
           const int vo = srow * kRowBytes + ((cslot ^ v_swz(row)) << 4);
           const int dst = (16 * (uniform(w) - 4) + 4 * q) * kRowBytes;   // scalar LDS offset
@@ -552,10 +568,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
 #pragma unroll
         for (int rg = 0; rg < 16; ++rg) mx = fmaxf(mx, st[kt][rg]);
       {
-        // the other half of the query's keys sits in lane l ^ 32
-        const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
-                                                         __builtin_bit_cast(unsigned, mx), false, false);
-        mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * sc;
+        // the other half of the query's keys sits in lane l ^ 32. The swap's two
+        // results are read by value (__uint_as_float): a __builtin_bit_cast of an
+        // element of the returned vector reads element 0 for either index (seen in
+        // the front end's IR), which dropped the other half from the page max.
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc;
       }
       const bool need = mx > m + kRescaleThreshold;
       const float mn = need ? mx : m;
