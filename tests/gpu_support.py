@@ -2,6 +2,10 @@
 (through its C ABI binding) and build the oracle's view of the same pool."""
 from __future__ import annotations
 
+import os
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -67,6 +71,81 @@ class OraclePool:
                 if r is not None:
                     vals[i] = r[g]
         return vals
+
+
+class SnapshotPool:
+    """The oracle's view of one pool, read from a copy of the generator's pool that
+    was taken on the device before any library kernel ran (``Run.k_pre`` /
+    ``Run.v_pre``), plus the oracle's own writes of the step.
+
+    ``check_append`` turns that copy into the expected post-append pool (the
+    pre-step values with the oracle's rows at the oracle's slots), so after it the
+    writes are already in place and applying them again changes nothing. Each
+    thread keeps the host copy of the last slot list it read, so the oracle's
+    per-KV-head reads of one row cost one device gather.
+    """
+
+    def __init__(self, pre: torch.Tensor, dtype: str):
+        self.pre = pre
+        self.dtype = dtype
+        self.writes = {}
+        self._local = threading.local()
+
+    def __setitem__(self, key, rows):
+        _, s, _ = key
+        self.writes[int(s)] = np.array(rows)
+
+    def __getitem__(self, key):
+        g, slots = key
+        slots = np.asarray(slots, dtype=np.int64)
+        c = getattr(self._local, "c", None)
+        if c is None or c[0].shape != slots.shape or not np.array_equal(c[0], slots):
+            idx = torch.as_tensor(slots, device=self.pre.device)
+            vals = host_values(self.pre.index_select(1, idx), self.dtype)
+            if self.writes:
+                for i, s in enumerate(slots.tolist()):
+                    r = self.writes.get(s)
+                    if r is not None:
+                        vals[:, i] = r
+            c = (slots.copy(), vals)
+            self._local.c = c
+        return c[1][g]
+
+
+def oracle_workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_parallel(fn, tokens):
+    """fn(tokens_subset) -> [len(subset), n] for interleaved subsets of ``tokens`` on
+    threads (the oracle's NumPy calls release the interpreter lock; BLAS runs one
+    thread per worker); the rows come back in the order of ``tokens``."""
+    from threadpoolctl import threadpool_limits
+    tokens = list(tokens)
+    n = max(1, min(oracle_workers(), len(tokens)))
+    parts_in = [tokens[i::n] for i in range(n)]
+    with threadpool_limits(1), ThreadPoolExecutor(n) as ex:
+        parts = list(ex.map(fn, parts_in))
+    out = np.empty((len(tokens), parts[0].shape[1]), dtype=np.float64)
+    for i in range(n):
+        out[i::n] = parts[i]
+    return out
+
+
+def report(name: str, got: np.ndarray, ref: np.ndarray, tol: float) -> float:
+    """Max and mean abs error and NaN count of got against ref; asserts no NaN and
+    max abs error <= tol. Returns the max abs error."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    d = np.abs(got.astype(np.float64) - ref)
+    n_nan = int(np.isnan(got).sum())
+    n_inf = int(np.isinf(got).sum())
+    mx = float(np.nanmax(d)) if d.size else 0.0
+    mean = float(np.nanmean(d)) if d.size else 0.0
+    print(f"[parity] {name}: {got.shape[0]} x {got.shape[1] if got.ndim > 1 else 1} outputs, "
+          f"max abs err {mx:.3e}, mean abs err {mean:.3e}, NaN {n_nan}, Inf {n_inf}", flush=True)
+    assert n_nan == 0 and n_inf == 0, f"{name}: non-finite outputs"
+    assert mx <= tol, f"{name}: max abs err {mx} > {tol}"
+    return mx
 
 
 class Run:
@@ -168,10 +247,33 @@ def oracle_append(w: W.Workload):
     return q_out, k_rows, v_rows, every_slot
 
 
-def oracle_pools(w: W.Workload, k_rows, v_rows, every_slot):
-    kp, vp = OraclePool(w, 0), OraclePool(w, 1)
+def oracle_pools(w: W.Workload, k_rows, v_rows, every_slot, run=None):
+    """The oracle's pools after the step's writes: from the run's pre-step copies
+    when it kept them (SnapshotPool), else regenerated on the host (OraclePool)."""
+    if run is not None and run.k_pre is not None:
+        kp, vp = SnapshotPool(run.k_pre, w.dtype), SnapshotPool(run.v_pre, w.dtype)
+    else:
+        kp, vp = OraclePool(w, 0), OraclePool(w, 1)
     O.apply_writes(kp, vp, every_slot, k_rows, v_rows)
     return kp, vp
+
+
+def oracle_decode(w: W.Workload, ref_q, kp, vp, rows=None):
+    """Oracle decode of the step's rows (all by default), threads over rows."""
+    P = w.n_prefill
+    rows = range(w.n_decode) if rows is None else rows
+    heads = {"n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads}
+    return oracle_parallel(lambda part: O.decode(ref_q[P:], w.dtype, kp, vp, w.dtype, w.decode_table,
+                                                 w.step_positions, W.SCALE, tokens=part, **heads), rows)
+
+
+def oracle_prefill(w: W.Workload, ref_q, kp, vp, toks=None):
+    """Oracle prefill of the step's prompt tokens (all by default), threads over tokens."""
+    P = w.n_prefill
+    toks = range(P) if toks is None else toks
+    heads = {"n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads}
+    return oracle_parallel(lambda part: O.prefill(ref_q[:P], w.dtype, kp, vp, w.dtype, w.table, w.rows,
+                                                  w.positions, W.SCALE, tokens=part, **heads), toks)
 
 
 def max_abs_err(got: np.ndarray, ref: np.ndarray) -> float:

@@ -3,8 +3,9 @@
 The kernels range-check every index they read from device memory: a page id
 outside the pool, a position outside the page table or the rotation table, a
 table row outside the table, a slot outside the pool. The token or row that
-carries it gets unspecified values (or none), and nothing is read or written
-outside the buffers. These tests corrupt a few rows and tokens of valid
+carries it gets NaN outputs when its position or row is out of range (as with a
+float32 pool) and unspecified values for a bad page, and nothing is read or
+written outside the buffers. These tests corrupt a few rows and tokens of valid
 workloads and check that every other row and token still matches the oracle
 bit for bit (q_out, pool bytes) or within the bfloat16 tolerance (attention).
 """
@@ -14,8 +15,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_support import (DEV, TOL_BF16, Run, bits, host_values, max_abs_err, oracle_append,
-                         oracle_pools)
+from gpu_support import (DEV, TOL_BF16, Run, bits, decode_workspace, host_values, lib, max_abs_err,
+                         oracle_append, oracle_pools)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,6 +63,14 @@ def test_decode_rows_with_bad_pages_and_positions():
     assert err <= TOL_BF16
     # a row with an out-of-pool page still attends over its other pages: finite
     assert torch.isfinite(run.dec_out[1]).all()
+    # rows whose position is outside the table get NaN outputs (as for a float32
+    # pool), written over whatever the output held
+    out = torch.zeros_like(run.dec_out)
+    lib().paged_decode_attn(run.q_out, run.k_pool, run.v_pool, tab, pos, W.SCALE, out,
+                            decode_workspace(run.k_pool, w.n_decode, w.pages_per_row))
+    torch.cuda.synchronize()
+    assert torch.isnan(out[5]).all() and torch.isnan(out[7]).all()
+    assert torch.isfinite(out[[0, 1, 2, 3, 4, 6]]).all()
 
 
 def test_prefill_tokens_with_bad_rows_positions_and_pages():
@@ -86,3 +95,11 @@ def test_prefill_tokens_with_bad_rows_positions_and_pages():
     err = max_abs_err(got, ref)
     print(f"[bad] prefill: {len(good)} valid tokens max abs err {err:.3e}", flush=True)
     assert err <= TOL_BF16
+    # tokens with an out-of-range position or row get NaN outputs (as for a float32 pool)
+    out = torch.zeros_like(run.pre_out)
+    ws = torch.zeros(lib().prefill_workspace_bytes(run.k_pool, 32, w.n_prefill), dtype=torch.uint8, device=DEV)
+    lib().paged_prefill_attn(run.q_out, run.k_pool, run.v_pool, t["table"], t["rows"], t["positions"], W.SCALE,
+                             out, ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[[125, 130, 145]]).all()
+    assert torch.isfinite(out[good]).all()

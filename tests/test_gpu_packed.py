@@ -87,3 +87,23 @@ def test_packed_history_does_not_change_the_result_bitwise():
         run.append()
         outs.append(_packed(run, seg))
     assert torch.equal(bits(outs[0]), bits(outs[1]))
+
+
+@pytest.mark.parametrize("fill_bits", [0x7FC0, 0x7F80, 0xFF80])
+def test_packed_ignores_non_finite_history_bitwise(fill_bits):
+    # history the packed form does not see may hold anything, NaN and +-Inf
+    # included (an uninitialised scratch pool of the training form): the result is
+    # bitwise the one over a clean history. The chunks start mid-page (300, 100,
+    # 64 + 90 tokens), so a run's first page mixes unseen history and its own keys.
+    w, seg = _workload("bf16", 44)
+    outs = []
+    for fill in (None, fill_bits):
+        run = Run(w, keep_pre=False)
+        if fill is not None:
+            val = torch.from_numpy(np.array([fill], np.uint16).view(np.int16)).view(torch.bfloat16).item()
+            run.k_pool.fill_(val)
+            run.v_pool.fill_(val)
+        run.append()
+        outs.append(_packed(run, seg))
+    assert torch.isfinite(outs[0]).all()
+    assert torch.equal(bits(outs[0]), bits(outs[1]))

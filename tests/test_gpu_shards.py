@@ -11,7 +11,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_support import TOL_BF16, Run, check_append, host_values, max_abs_err, oracle_append, oracle_pools
+from gpu_support import (TOL_BF16, Run, check_append, oracle_append, oracle_decode, oracle_pools, oracle_prefill,
+                         report)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,30 +45,18 @@ def test_mixed_step_at_a_shard_shape(kv):
     ref_p = O.prefill(ref_q[:P], w.dtype, kp, vp, w.dtype, w.table, w.rows, w.positions, W.SCALE, **_heads(w))
     ref_d = O.decode(ref_q[P:], w.dtype, kp, vp, w.dtype, w.decode_table, w.step_positions, W.SCALE,
                      **_heads(w))
-    ep = max_abs_err(run.pre_out.cpu().numpy(), ref_p)
-    ed = max_abs_err(run.dec_out.cpu().numpy(), ref_d)
-    print(f"[shard] prefill err {ep:.3e} decode err {ed:.3e}", flush=True)
-    assert ep <= TOL_BF16 and ed <= TOL_BF16
+    report(f"shard {kv} KV heads prefill", run.pre_out.cpu().numpy(), ref_p, TOL_BF16)
+    report(f"shard {kv} KV heads decode", run.dec_out.cpu().numpy(), ref_d, TOL_BF16)
 
 
 def test_standard_step_one_kv_head():
-    # the mixed-step workload as one of 8 shards: same rows, positions and pages, 1 KV head
+    # the mixed-step workload as one of 8 shards: same rows, positions and pages,
+    # 1 KV head; every output
     w = W.config(4, kv_heads=1)
-    run = Run(w, keep_pre=False)
+    run = Run(w)
     run.step()
     ref_q, k_rows, v_rows, slots = oracle_append(w)
-    assert np.array_equal(host_values(run.q_out, w.dtype), ref_q), "q_out bytes differ"
-    kp, vp = oracle_pools(w, k_rows, v_rows, slots)
-    rng = np.random.default_rng(64)
-    P, R = w.n_prefill, w.n_decode
-    rows = sorted(set([int(np.argmax(w.step_positions))] + [int(x) for x in rng.choice(R, 7, replace=False)]))
-    ref_d = O.decode(ref_q[P:], w.dtype, kp, vp, w.dtype, w.decode_table, w.step_positions, W.SCALE,
-                     tokens=rows, **_heads(w))
-    ed = max_abs_err(run.dec_out[rows].cpu().numpy(), ref_d)
-    toks = sorted(set([0, 2047, 2048, P - 1] + [int(x) for x in rng.choice(P, 60, replace=False)]))
-    ref_p = O.prefill(ref_q[:P], w.dtype, kp, vp, w.dtype, w.table, w.rows, w.positions, W.SCALE,
-                      tokens=toks, **_heads(w))
-    ep = max_abs_err(run.pre_out[toks].cpu().numpy(), ref_p)
-    print(f"[shard] step at 1 KV head: decode rows {len(rows)} err {ed:.3e}, prefill tokens {len(toks)} "
-          f"err {ep:.3e}", flush=True)
-    assert ed <= TOL_BF16 and ep <= TOL_BF16
+    check_append(run, ref_q, k_rows, v_rows, slots)
+    kp, vp = oracle_pools(w, k_rows, v_rows, slots, run)
+    report("step at 1 KV head decode", run.dec_out.cpu().numpy(), oracle_decode(w, ref_q, kp, vp), TOL_BF16)
+    report("step at 1 KV head prefill", run.pre_out.cpu().numpy(), oracle_prefill(w, ref_q, kp, vp), TOL_BF16)

@@ -19,10 +19,12 @@ head_dim 128, pages of 64 positions, at most 40960 positions per row):
 
 Pool contents before the step ("history") come from a counter-based hash of
 (seed, k-or-v, kv head, slot, element) so that any page can be regenerated on
-the host without copying the pool back. Each value is an Irwin-Hall sum of four
-uniform bytes, centred and scaled by 1/128 (mean 0, standard deviation 1.155,
-range [-3.98, 3.98]), exact in float32. Slots that hold neither history nor a
-write of the step are NaN so that a wrong read shows up in the output.
+the host without copying the pool back. The top 16 bits of the hash pick one of
+65536 standard normal quantiles (at probabilities (i + 1/2) / 65536, float32), so
+the history is N(0, 1) to within that discretisation (tails to about 4.3), and
+the same table lookup gives identical values on the CPU and on the GPU. Slots
+that hold neither history nor a write of the step are NaN so that a wrong read
+shows up in the output.
 """
 from __future__ import annotations
 
@@ -117,7 +119,7 @@ def _bf16_bits(x: np.ndarray) -> np.ndarray:
 def build(name: str, seed: int, dtype: str, num_pages: int, pages_per_row: int,
           n_table_rows: int, chunks=(), decode=(), decode_row0: int = 0,
           shared_prefix_pages: int = 0, reserve_page0: bool = True,
-          n_kv_heads: int = NUM_KV_HEADS) -> Workload:
+          n_kv_heads: int = NUM_KV_HEADS, gain_range=(0.5, 1.5)) -> Workload:
     """General builder.
 
     ``chunks``: sequence of (row, first_position, length) prompt chunks, packed
@@ -127,6 +129,8 @@ def build(name: str, seed: int, dtype: str, num_pages: int, pages_per_row: int,
     row uses min(shared, position // 64) of them, so the page it writes is its own.
     ``n_kv_heads``: KV heads of the workload (4 query heads each); fewer than 8 is
     one GPU's share of the heads when they are sharded over 8 / n_kv_heads GPUs.
+    ``gain_range``: the QK-norm gains are uniform in it ((0.5, 1.5) by default;
+    large gains give wide score ranges).
     """
     rng = np.random.default_rng(seed)
     need = {}      # row -> number of positions the row spans after the step
@@ -169,8 +173,8 @@ def build(name: str, seed: int, dtype: str, num_pages: int, pages_per_row: int,
     q = rng.standard_normal((n_tok, n_q_heads * HEAD_DIM), dtype=np.float32)
     k = rng.standard_normal((n_tok, n_kv_heads * HEAD_DIM), dtype=np.float32)
     v = rng.standard_normal((n_tok, n_kv_heads * HEAD_DIM), dtype=np.float32)
-    q_gain = rng.uniform(0.5, 1.5, HEAD_DIM).astype(np.float32)
-    k_gain = rng.uniform(0.5, 1.5, HEAD_DIM).astype(np.float32)
+    q_gain = rng.uniform(gain_range[0], gain_range[1], HEAD_DIM).astype(np.float32)
+    k_gain = rng.uniform(gain_range[0], gain_range[1], HEAD_DIM).astype(np.float32)
     if dtype == "bf16":
         q, k, v = _bf16_bits(q), _bf16_bits(k), _bf16_bits(v)
     history = sorted(hist.items())
@@ -218,6 +222,20 @@ def config(i: int, seed: int | None = None, kv_heads: int = NUM_KV_HEADS) -> Wor
 # --------------------------------------------------------------------------
 
 _M32 = 0xFFFFFFFF
+_NORMAL_TABLE = None
+_TABLE_ON = {}   # device -> the quantile table as a torch tensor there
+
+
+def normal_quantiles() -> np.ndarray:
+    """float32 [65536]: the standard normal quantile at (i + 1/2) / 65536."""
+    global _NORMAL_TABLE
+    if _NORMAL_TABLE is None:
+        from statistics import NormalDist
+        nd = NormalDist()
+        _NORMAL_TABLE = np.array([nd.inv_cdf((i + 0.5) / 65536.0) for i in range(65536)],
+                                 dtype=np.float64).astype(np.float32)
+        _NORMAL_TABLE.flags.writeable = False
+    return _NORMAL_TABLE
 
 
 def _mix32(x):
@@ -240,8 +258,10 @@ def history_values(seed: int, which: int, kv_head: int, slots, device="cpu"):
     key = int(_mix32(np.int64(((seed * 2 + which) * 64 + kv_head + 1) & _M32)))
     idx = s[:, None] * HEAD_DIM + torch.arange(HEAD_DIM, device=device, dtype=torch.int64)[None, :]
     h = _mix32(_mix32(idx & _M32) ^ key)
-    total = (h & 255) + ((h >> 8) & 255) + ((h >> 16) & 255) + ((h >> 24) & 255)
-    return (total - 510).to(torch.float32) * (1.0 / 128.0)
+    dev = str(torch.device(device))
+    if dev not in _TABLE_ON:
+        _TABLE_ON[dev] = torch.from_numpy(normal_quantiles().copy()).to(device)
+    return _TABLE_ON[dev][h >> 16]
 
 
 def torch_dtype(dtype: str):
