@@ -421,27 +421,141 @@ def test_partial_rotary_leaves_the_tail_and_rotates_the_head_bitwise():
 
 
 def test_partial_rotary_scores_depend_on_relative_position_of_rotated_part():
-    # <R(m)q, R(n)k> over the rotated part depends on m - n only; the tail adds a
-    # position-free term
+    # <R(m)q, R(n)k> through the oracle's rope_rotate with rotary_dim R depends on
+    # m - n only (up to float32 rounding); the unrotated tail adds the same
+    # position-free term at any positions
     rng = _rng(24)
     R = 32
-    q = rng.standard_normal(128)
-    k = rng.standard_normal(128)
+    q = rng.standard_normal(128).astype(np.float32)
+    k = rng.standard_normal(128).astype(np.float32)
 
     def rot(x, pos):
-        inv = np.array(O.rope_inv_freq(O.ROPE_THETA, R))
-        a = pos * inv
-        c, s = np.cos(a), np.sin(a)
-        h = R // 2
-        out = x.copy()
-        out[:h] = x[:h] * c - x[h:R] * s
-        out[h:R] = x[h:R] * c + x[:h] * s
-        return out
+        c, s = O.rope_row(O.ROPE_THETA, pos, R)
+        return O.rope_rotate(x, c, s, R).astype(np.float64)
 
     d1 = rot(q, 100) @ rot(k, 40)
     d2 = rot(q, 1060) @ rot(k, 1000)
-    assert abs(d1 - d2) < 1e-9
-    assert abs((rot(q, 5)[R:] @ rot(k, 900)[R:]) - (q[R:] @ k[R:])) == 0.0
+    assert abs(d1 - d2) < 1e-4
+    assert abs(d1 - rot(q, 40) @ rot(k, 100)) > 1e-3       # the sign of m - n matters
+    tail = q[R:].astype(np.float64) @ k[R:].astype(np.float64)
+    assert rot(q, 5)[R:] @ rot(k, 900)[R:] == tail
+    # against the complex rotation of the first R elements in float64
+    c, s = O.rope_row(O.ROPE_THETA, 777, R)
+    z = (q[:R // 2] + 1j * q[R // 2:R]) * (c.astype(np.float64) + 1j * s.astype(np.float64))
+    np.testing.assert_allclose(rot(q, 777)[:R], np.concatenate([z.real, z.imag]), atol=2e-6)
+
+
+# ------------------------------------------------- the pinned float32 order
+# The pages fix no intermediate precision for QK-norm; the oracle pins one float32
+# order (neighbours-first pairwise sum of p_l = x_l^2 + x_{l+64}^2, an odd last
+# element carried up). Below, a scalar transcription of that order in plain
+# Python over numpy float32 scalars, and three other plausible orders. The inputs
+# spread their squares over many octaves, so the orders round differently; the
+# oracle must equal the pinned one bit for bit and differ from each other one.
+
+F32 = np.float32
+
+
+def _tree_neighbours(vals):
+    vals = list(vals)
+    while len(vals) > 1:
+        nxt = [F32(vals[i] + vals[i + 1]) for i in range(0, len(vals) - 1, 2)]
+        if len(vals) % 2:
+            nxt.append(vals[-1])
+        vals = nxt
+    return vals[0]
+
+
+def _xor_butterfly(vals):
+    # s_l <- s_l + s_{l xor k} for k = 32, 16, ..., 1 over 64 lanes; lane 0's value
+    s = list(vals)
+    k = len(s) // 2
+    while k >= 1:
+        s = [F32(s[l] + s[l ^ k]) for l in range(len(s))]
+        k //= 2
+    return s[0]
+
+
+def _sequential(vals):
+    acc = F32(0.0)
+    for v in vals:
+        acc = F32(acc + v)
+    return acc
+
+
+def _numpy_sum(vals):
+    return np.sum(np.array(vals, dtype=np.float32))
+
+
+def _scalar_norm(x, g, eps, order):
+    """One head (or, with ``order`` applied to head sums, see below) by the recipe."""
+    d = len(x)
+    half = d // 2
+    p = [F32(F32(x[l] * x[l]) + F32(x[l + half] * x[l + half])) for l in range(half)]
+    ss = order(p)
+    ms = F32(ss / F32(d))
+    r = F32(F32(1.0) / np.sqrt(F32(ms + F32(eps))))
+    return np.array([F32(F32(x[i] * r) * g[i]) for i in range(d)], dtype=np.float32)
+
+
+def _octave_vectors(rng, n, d=128):
+    mag = np.exp2(rng.uniform(-8, 8, size=(n, d)))
+    return (rng.standard_normal((n, d)) * mag).astype(np.float32)
+
+
+def test_qk_norm_float32_order_is_the_pinned_one_bitwise():
+    rng = _rng(30)
+    x = _octave_vectors(rng, 200)
+    g = rng.uniform(0.5, 1.5, 128).astype(np.float32)
+    got = O.qk_norm(x, g, 1e-6)
+    differ = {"butterfly": 0, "sequential": 0, "numpy": 0}
+    for i in range(len(x)):
+        pinned = _scalar_norm(x[i], g, 1e-6, _tree_neighbours)
+        assert np.array_equal(got[i].view(np.uint32), pinned.view(np.uint32)), i
+        for name, order in (("butterfly", _xor_butterfly), ("sequential", _sequential),
+                            ("numpy", _numpy_sum)):
+            differ[name] += not np.array_equal(_scalar_norm(x[i], g, 1e-6, order).view(np.uint32),
+                                               pinned.view(np.uint32))
+    # each other order gives other bits on these inputs, so the check discriminates
+    assert all(c > 0 for c in differ.values()), differ
+
+
+def _scalar_norm_whole(x, g, eps, order=_tree_neighbours):
+    """All heads of one token: per-head sums of squares by the recipe, then the head
+    sums by ``order``, ms = total / (H*D)."""
+    h, d = x.shape
+    half = d // 2
+    heads = [_tree_neighbours([F32(F32(x[j, l] * x[j, l]) + F32(x[j, l + half] * x[j, l + half]))
+                               for l in range(half)]) for j in range(h)]
+    total = order(heads)
+    ms = F32(total / F32(h * d))
+    r = F32(F32(1.0) / np.sqrt(F32(ms + F32(eps))))
+    gg = np.asarray(g, np.float32).reshape(h, d)
+    return np.array([[F32(F32(x[j, i] * r) * gg[j, i]) for i in range(d)] for j in range(h)], np.float32)
+
+
+@pytest.mark.parametrize("heads", [3, 5, 12, 17, 20, 40, 68, 160])
+def test_qk_norm_whole_at_odd_and_uneven_head_counts(heads):
+    # the head counts the whole-vector variant is run at on the GPU (query heads
+    # 12, 20, 68, 160; KV heads 3, 5, 17, 40): pinned order bit for bit, torch
+    # rms_norm over all heads in float64, and a sequential head sum differs
+    rng = _rng(31 + heads)
+    n = 12
+    x = (rng.standard_normal((n, heads, 128)) *
+         np.exp2(rng.uniform(-10, 10, size=(n, heads, 1)))).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, heads * 128).astype(np.float32)
+    got = O.qk_norm_whole(x, g, 1e-6)
+    seq_differs = 0
+    for t in range(n):
+        pinned = _scalar_norm_whole(x[t], g, 1e-6)
+        assert np.array_equal(got[t].view(np.uint32), pinned.view(np.uint32)), t
+        seq_differs += not np.array_equal(_scalar_norm_whole(x[t], g, 1e-6, _sequential).view(np.uint32),
+                                          pinned.view(np.uint32))
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x.reshape(n, -1)).double(), (heads * 128,),
+                                       weight=torch.from_numpy(g).double(), eps=1e-6).numpy()
+    np.testing.assert_allclose(got.reshape(n, -1), ref, rtol=2e-6, atol=1e-30)
+    if heads >= 5:
+        assert seq_differs > 0
 
 
 def test_output_gate_closed_forms():
