@@ -61,7 +61,8 @@ typedef enum {
   QKR_EINVAL = -1,          /* null pointer, negative count, bad divisibility  */
   QKR_EUNSUPPORTED = -2,    /* head_dim != 128, page_size != 64, dtype combo    */
   QKR_EWORKSPACE = -3,      /* workspace missing or smaller than required       */
-  QKR_ELAUNCH = -4          /* the HIP runtime reported an error on launch      */
+  QKR_ELAUNCH = -4,         /* the HIP runtime reported an error on launch      */
+  QKR_EDATA = -5            /* qkr_check_indices found out-of-range device data */
 } qkr_status;
 
 /* Shape of the paged pool. num_q_heads % num_kv_heads == 0 and the group size
@@ -352,6 +353,50 @@ int step_paged(void* stream, const qkr_pool* pool, int32_t n_prefill, int32_t n_
                float* prefill_out, float* decode_out, void* workspace, size_t workspace_bytes);
 
 size_t step_paged_workspace(const qkr_pool* pool, int32_t n_prefill, int32_t n_decode, int32_t pages_per_row);
+
+/*
+ * qkr_check_indices -- validate the device-side indices of a step before it runs
+ * (nest "models/qwen3-8b/files", README: every name, shape and dtype is checked
+ * before anything runs; Entries table: a row's positions lie in the pages its
+ * table row lists). The append and attention calls range-check every index they
+ * form and skip or mask what is out of range, so bad data passes there without a
+ * diagnosis; this call counts it.
+ *
+ * Queries: n_tokens prompt tokens (rows, positions, and optionally slots: device
+ * int32 [n_tokens]) and n_decode decode rows (step_positions: device int32
+ * [n_decode]; decode row b uses table row decode_row0 + b). For each query it
+ * counts, into counts[QKR_CHECK_*] (device int32 [QKR_CHECK_COUNTS]):
+ *   QKR_CHECK_ROW           prompt tokens with rows[p] outside [0, n_table_rows);
+ *   QKR_CHECK_POSITION      queries with a position outside [0, pages_per_row*64)
+ *                           or, when rope_rows > 0, outside [0, rope_rows);
+ *   QKR_CHECK_PAGE          queries with a valid row and position one of whose
+ *                           visible pages (table entries 0 .. position / 64 of
+ *                           its row) is outside [0, num_pages);
+ *   QKR_CHECK_SLOT_RANGE    prompt tokens with slots[p] >= num_pages*64
+ *                           (negative slots are padding and not counted);
+ *   QKR_CHECK_SLOT_MISMATCH prompt tokens with a valid row and position whose
+ *                           slots[p] >= 0 differs from table[rows[p]][pos / 64]*64
+ *                           + pos % 64.
+ * Two real tokens writing one slot are not detected. decode_row0 + n_decode <=
+ * n_table_rows is checked on the host (QKR_EINVAL).
+ *
+ * wait == 0: the counts are zeroed and filled on `stream` (a fill kernel and one
+ * check kernel); nothing allocates and nothing synchronises; the counts are valid
+ * once the stream reaches them. wait != 0: the call then waits for `stream`,
+ * reads the counts and returns QKR_EDATA if any is non-zero (QKR_OK otherwise).
+ * counts must not be shared by calls that may overlap.
+ */
+#define QKR_CHECK_ROW 0
+#define QKR_CHECK_POSITION 1
+#define QKR_CHECK_PAGE 2
+#define QKR_CHECK_SLOT_RANGE 3
+#define QKR_CHECK_SLOT_MISMATCH 4
+#define QKR_CHECK_COUNTS 8
+int qkr_check_indices(void* stream, const qkr_pool* pool,
+                      const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
+                      int32_t n_tokens, const int32_t* rows, const int32_t* positions, const int32_t* slots,
+                      int32_t n_decode, const int32_t* step_positions, int32_t decode_row0,
+                      int32_t rope_rows, int32_t* counts, int32_t wait);
 
 /*
  * qkr_rope_table -- host helper: the RoPE cos/sin table (host memory).

@@ -18,6 +18,9 @@ QKR_BF16 = 1
 HEAD_DIM = 128
 PAGE_SIZE = 64
 NOALLOC_MAX_ROW_HEADS = 98304   # QKR_NOALLOC_MAX_ROW_HEADS: rows x KV heads of paged_decode_attn_noalloc
+QKR_EDATA = -5
+CHECK_NAMES = ("row", "position", "page", "slot_range", "slot_mismatch")   # QKR_CHECK_* order
+CHECK_COUNTS = 8
 
 EXPORTED = (
     "qknorm_rope_append",
@@ -34,6 +37,7 @@ EXPORTED = (
     "packed_prefill_attn_workspace",
     "step_paged",
     "step_paged_workspace",
+    "qkr_check_indices",
     "qkr_rope_table",
     "qkr_status_str",
     "qkr_last_error",
@@ -121,6 +125,8 @@ def _load():
                                vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, sz]
     lib.step_paged_workspace.restype = sz
     lib.step_paged_workspace.argtypes = [pool_p, i32, i32, i32]
+    lib.qkr_check_indices.restype = ctypes.c_int
+    lib.qkr_check_indices.argtypes = [vp, pool_p, vp, i32, i32, i32, vp, vp, vp, i32, vp, i32, i32, vp, i32]
     lib.qkr_rope_table.restype = ctypes.c_int
     lib.qkr_rope_table.argtypes = [ctypes.c_double, i32, i32, vp, vp]
     lib.qkr_status_str.restype = ctypes.c_char_p
@@ -366,6 +372,35 @@ def step_paged(q, k, v, q_gain, k_gain, rope_cos, rope_sin, positions, rows, slo
         _ptr(decode_out, "decode_out", torch.float32, R * n_q * HEAD_DIM) if R else None,
         _ptr(workspace, "workspace"), ws_bytes)
     _check(st, "step_paged")
+
+
+def check_indices(k_pool, num_q_heads: int, table, rows=None, positions=None, slots=None, step_positions=None,
+                  decode_row0: int = 0, rope_rows: int = 0, counts=None, wait: bool = True, stream=None):
+    """qkr_check_indices: count out-of-range rows, positions, visited page ids and
+    slots, and slots that differ from their row's page table, for prompt tokens
+    (rows, positions, slots) and decode rows (step_positions, table rows
+    decode_row0 + b). Returns (status, counts): with wait, status is 0 or
+    QKR_EDATA and counts a dict; without it, status 0 and counts the device
+    int32 tensor the counts land in (nothing synchronises)."""
+    import torch
+    pool = pool_desc(k_pool, num_q_heads)
+    P = 0 if positions is None else int(positions.numel())
+    R = 0 if step_positions is None else int(step_positions.numel())
+    if counts is None:
+        counts = torch.zeros(CHECK_COUNTS, dtype=torch.int32, device=table.device)
+    st = LIB.qkr_check_indices(
+        _stream(stream), ctypes.byref(pool), _ptr(table, "table", torch.int32), int(table.shape[0]),
+        int(table.shape[-1]), P, _ptr(rows, "rows", torch.int32, P) if P else None,
+        _ptr(positions, "positions", torch.int32, P) if P else None,
+        _ptr(slots, "slots", torch.int32, P) if (P and slots is not None) else None,
+        R, _ptr(step_positions, "step_positions", torch.int32, R) if R else None, int(decode_row0),
+        int(rope_rows), _ptr(counts, "counts", torch.int32, CHECK_COUNTS), 1 if wait else 0)
+    if st not in (0, QKR_EDATA):
+        _check(st, "qkr_check_indices")
+    if not wait:
+        return st, counts
+    c = counts.cpu().tolist()
+    return st, {name: int(c[i]) for i, name in enumerate(CHECK_NAMES)}
 
 
 def version() -> int:

@@ -33,6 +33,7 @@ SOURCES = {
     "prefill.hip": [],
     "generic.hip": [],
     "step.hip": [],
+    "check.hip": [],
     "api.cpp": ["-ffp-contract=off"],
 }
 

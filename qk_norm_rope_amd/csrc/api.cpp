@@ -111,6 +111,7 @@ const char* qkr_status_str(int s) {
     case QKR_EUNSUPPORTED: return "unsupported shape or dtype";
     case QKR_EWORKSPACE: return "workspace missing or too small";
     case QKR_ELAUNCH: return "kernel launch failed";
+    case QKR_EDATA: return "device data out of range";
     default: return "unknown status";
   }
 }
@@ -328,6 +329,59 @@ int packed_prefill_attn(void* stream, const qkr_pool* pool, int32_t n_tokens,
   return packed_prefill_attn_ex(stream, pool, n_tokens, q, k_pool, v_pool, table, n_table_rows,
                                 pages_per_row, rows, positions, segments, scale, out, workspace,
                                 workspace_bytes, nullptr);
+}
+
+int qkr_check_indices(void* stream, const qkr_pool* pool,
+                      const int32_t* table, int32_t n_table_rows, int32_t pages_per_row,
+                      int32_t n_tokens, const int32_t* rows, const int32_t* positions, const int32_t* slots,
+                      int32_t n_decode, const int32_t* step_positions, int32_t decode_row0,
+                      int32_t rope_rows, int32_t* counts, int32_t wait) {
+  static_assert(QKR_CHECK_ROW == qknr::kCheckRow && QKR_CHECK_POSITION == qknr::kCheckPosition &&
+                    QKR_CHECK_PAGE == qknr::kCheckPage && QKR_CHECK_SLOT_RANGE == qknr::kCheckSlotRange &&
+                    QKR_CHECK_SLOT_MISMATCH == qknr::kCheckSlotMismatch && QKR_CHECK_COUNTS == qknr::kCheckCounts,
+                "count layout");
+  int st = check_pool(pool);
+  if (st != QKR_OK) return st;
+  if (n_tokens < 0 || n_decode < 0 || rope_rows < 0) return QKR_EINVAL;
+  if (!counts || !table || n_table_rows <= 0 || pages_per_row <= 0) return QKR_EINVAL;
+  if (n_tokens > 0 && (!rows || !positions)) return QKR_EINVAL;
+  if (n_decode > 0) {
+    if (!step_positions) return QKR_EINVAL;
+    if (decode_row0 < 0 || (int64_t)decode_row0 + n_decode > n_table_rows) return QKR_EINVAL;
+  }
+  if ((int64_t)n_tokens + n_decode > (int64_t)1 << 30) return QKR_EUNSUPPORTED;
+  qknr::CheckArgs a;
+  a.table = table;
+  a.n_table_rows = n_table_rows;
+  a.pages_per_row = pages_per_row;
+  a.num_pages = pool->num_pages;
+  a.n_tokens = n_tokens;
+  a.rows = rows;
+  a.positions = positions;
+  a.slots = slots;
+  a.n_decode = n_decode;
+  a.step_positions = step_positions;
+  a.decode_row0 = decode_row0;
+  a.rope_rows = rope_rows;
+  a.counts = counts;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_status(qknr::launch_check_indices(s, a));
+  if (st != QKR_OK || !wait) return st;
+  int32_t host[QKR_CHECK_COUNTS];
+  st = launch_status(hipMemcpyAsync(host, counts, sizeof(host), hipMemcpyDeviceToHost, s));
+  if (st != QKR_OK) return st;
+  st = launch_status(hipStreamSynchronize(s));
+  if (st != QKR_OK) return st;
+  for (int i = 0; i < QKR_CHECK_COUNTS; ++i)
+    if (host[i] != 0) {
+      snprintf(g_last_error, sizeof(g_last_error),
+               "qkr_check_indices: %d bad rows, %d bad positions, %d queries with a page outside the pool, "
+               "%d slots outside the pool, %d slots that differ from their row's page table",
+               host[QKR_CHECK_ROW], host[QKR_CHECK_POSITION], host[QKR_CHECK_PAGE], host[QKR_CHECK_SLOT_RANGE],
+               host[QKR_CHECK_SLOT_MISMATCH]);
+      return QKR_EDATA;
+    }
+  return QKR_OK;
 }
 
 size_t step_paged_workspace(const qkr_pool* pool, int32_t n_prefill, int32_t n_decode, int32_t pages_per_row) {

@@ -92,6 +92,23 @@ struct StepArgs {
   void* workspace;
   int decode_slices = 0;   // decode work items (0: twice the resident workgroups)
 };
+// Device-data validation: counts of index violations, kCheckCounts ints in device
+// memory (the order of QKR_CHECK_* in qknr.h).
+enum : int { kCheckRow = 0, kCheckPosition, kCheckPage, kCheckSlotRange, kCheckSlotMismatch, kCheckCounts = 8 };
+struct CheckArgs {
+  const int32_t* table;
+  int n_table_rows, pages_per_row;
+  int64_t num_pages;
+  int n_tokens;
+  const int32_t *rows, *positions, *slots;
+  int n_decode;
+  const int32_t* step_positions;
+  int decode_row0;
+  int rope_rows;   // 0: no rotation-table limit
+  int32_t* counts;
+};
+hipError_t launch_check_indices(hipStream_t stream, const CheckArgs& a);
+
 size_t step_workspace_bytes(int n_prefill, int n_decode, int n_kv_heads, int pages_per_row);
 // Whether step_paged launches its kernel (off until the kernel has passed its GPU tests).
 bool step_enabled();

@@ -258,3 +258,25 @@ def test_noalloc_decode_host_checks():
     p4 = _pool(num_q_heads=16, num_kv_heads=4)
     assert lib.paged_decode_attn_noalloc(None, ctypes.byref(p4), 12289, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
                                          0.1, FAKE) == -2
+
+
+def _check(pool, **kw):
+    a = dict(table=FAKE, n_table_rows=4, ppr=8, n=3, rows=FAKE, pos=FAKE, slots=FAKE, r=2, spos=FAKE,
+             row0=2, rope_rows=100, counts=FAKE, wait=0)
+    a.update(kw)
+    return L.LIB.qkr_check_indices(None, ctypes.byref(pool), a["table"], a["n_table_rows"], a["ppr"], a["n"],
+                                   a["rows"], a["pos"], a["slots"], a["r"], a["spos"], a["row0"],
+                                   a["rope_rows"], a["counts"], a["wait"])
+
+
+def test_check_indices_host_checks():
+    pool = _pool()
+    assert _check(pool, counts=None) == -1
+    assert _check(pool, table=None) == -1
+    assert _check(pool, rows=None) == -1               # prompt tokens need rows and positions
+    assert _check(pool, spos=None) == -1               # decode rows need positions
+    assert _check(pool, row0=3) == -1                  # decode rows 3..4 of a 4-row table
+    assert _check(pool, n=-1) == -1
+    assert _check(pool, rope_rows=-1) == -1
+    assert _check(_pool(head_dim=64)) == -2
+    assert Q.status_str(L.QKR_EDATA) == "device data out of range"
