@@ -337,10 +337,6 @@ int packed_prefill_attn_ex(void* stream, const qkr_pool* pool, int32_t n_tokens,
  *   exhausts; words 6 and 7 then hold the counts it saw); the library never
  *   clears those words.
  * Device indices are range-checked as in the three calls above.
- *
- * In this version of the library the single-launch kernel is switched off:
- * after the argument checks above, the call returns QKR_EUNSUPPORTED
- * (qkr_last_error says so) and enqueues nothing. Use the three calls.
  */
 int step_paged(void* stream, const qkr_pool* pool, int32_t n_prefill, int32_t n_decode,
                const void* q, const void* k, const void* v, int32_t in_dtype,

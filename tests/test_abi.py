@@ -211,14 +211,6 @@ def test_step_host_checks():
     assert L.LIB.step_paged_workspace(ctypes.byref(pool), 100, 0, 4) < need
 
 
-def test_step_is_switched_off_after_its_checks():
-    # valid arguments reach the switch: nothing is enqueued, the status says unsupported
-    pool = _pool()
-    need = L.LIB.step_paged_workspace(ctypes.byref(pool), 100, 2, 4)
-    assert _step(pool, ws_bytes=need) == -2
-    assert "switched off" in L.last_error()
-
-
 def test_size_limits_host_checks():
     pool = _pool()
     lib = L.LIB
