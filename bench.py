@@ -204,6 +204,40 @@ def rates(w, times):
     return out
 
 
+def measure_fused(step, stream, steps, scratch):
+    """The same step through step_paged (one launch), timed like the three calls:
+    one event window per step, flushed before each when ``scratch`` is given, else
+    back to back."""
+    import torch
+    Q, W, w, t = step.Q, step.W, step.w, step.t
+    P, R = step.P, step.R
+    ws = torch.zeros(max(1, Q.step_workspace_bytes(step.k_pool, w.n_q_heads, P, R, w.pages_per_row)),
+                     dtype=torch.uint8, device=step.q_out.device)
+
+    def f():
+        Q.step_paged(t["q"], t["k"], t["v"], t["q_gain"], t["k_gain"], step.cos, step.sin,
+                     t["positions"] if P else None, t["rows"] if P else None, t["slots"] if P else None,
+                     t["step_positions"] if R else None, t["table"], w.decode_row0, W.SCALE,
+                     step.q_out, step.k_pool, step.v_pool, step.pre_out, step.dec_out, ws)
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        if scratch is not None:
+            scratch.amax()
+        a.record(stream)
+        f()
+        b.record(stream)
+    torch.cuda.synchronize()
+    if scratch is not None:
+        ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    else:
+        ms = evs[0][0].elapsed_time(evs[-1][1]) / steps
+    fault = int(ws[20:24].view(torch.int32).item())
+    return {"ms_per_step": round(ms, 4), "kernel": "step_paged_kernel", "launches": 1, "wait_gave_up": fault}
+
+
 def measure_append_steady(step, stream, reps=50):
     """The step's append, launched back to back (its in-step event window also holds
     the launch gap after the previous step's last kernel)."""
@@ -535,6 +569,7 @@ def main():
         for k, v in wr.items():
             warm[k] = {"gbs" if "gbs" in v else "tflops": v.get("gbs", v.get("tflops")),
                        "ms_per_launch": v["ms_per_launch"]}
+    fused = measure_fused(step, stream, args.steps, scratch) if extras else None
     app_steady_ms = measure_append_steady(step, stream) if extras else None
     packed = measure_packed(step, stream) if (step.P and extras) else None
     variants = measure_variants(step, stream) if extras else None
@@ -588,6 +623,10 @@ def main():
         work = algorithmic_work(w)
         result["append"]["steady_gbs"] = round(work["append_bytes"] / (app_steady_ms * 1e-3) / 1e9, 2)
         result["append"]["steady_ms_per_launch"] = round(app_steady_ms, 5)
+    if fused is not None:
+        fused["ms_per_step_three_calls"] = round(step_ms, 4)
+        fused["speedup"] = round(step_ms / fused["ms_per_step"], 4)
+        result["fused_step"] = fused
     if warm is not None:
         result["warm"] = warm
     if others is not None:
