@@ -16,6 +16,244 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(DecodeParams P) 
   decode_slice<4>(P, blockIdx.x, gridDim.x, s_prefix, threadIdx.x);
 }
 
+// Small batches (few rows x short tables): one workgroup of 4 waves per (row b, KV
+// head g, chunk c of CP pages), the grid fixed by the host as rows x KV heads x
+// ceil(pages_per_row / CP). A workgroup knows its row before it reads anything,
+// so the row's position, the query operand and the chunk's page ids travel in one
+// memory round trip, and then all CP pages of the chunk are in flight at once
+// (the stream-K kernel needs a round trip for the positions, one for the prefix
+// over the rows and then fetches two pages per wave at a time). A chunk past the
+// row's last page leaves at once; a row of one chunk is written directly; the
+// chunks of a longer row leave partial states that the last one to finish merges
+// in chunk order (deterministic). Wave w takes keys 16w..16w+15 of every page,
+// with the same per-page arithmetic as decode_slice.
+template <int CP>
+__device__ __forceinline__ void decode_chunk(const DecodeParams& P, const int blk, const int C, const int tid) {
+  __shared__ __attribute__((aligned(16))) float s_p[4][16][kGroup];
+  __shared__ float s_m[4][kGroup], s_l[4][kGroup];
+  __shared__ __attribute__((aligned(16))) float s_acc[4][kGroup][kHeadDim];
+  __shared__ int s_last;
+  constexpr int TPH = 256 / kGroup;     // threads per head in the merge
+  constexpr int DPT = kHeadDim / TPH;   // dimensions per thread in the merge (2)
+  const int w = tid >> 6, l = tid & 63, hr = l & 15, G4 = l >> 4;
+  const int c = blk % C;
+  const int bg = blk / C;   // (row, KV head) segment
+  const int g = bg % P.n_kv, b = bg / P.n_kv;
+  const int n_q = P.n_kv * kGroup;
+  const int64_t pool_slots = P.num_pages * kPageSize;
+
+  // ---- one round trip: position, query operand, the chunk's page ids
+  const int pos = P.positions[b];
+  bf16x8 qa[4];
+  if (hr < kGroup) {
+    // rows 0..3 = heads 4g..4g+3; k-slot 8*G4+i of step st = dim 8*(4*st+G4)+i
+    const uint16_t* qp = P.q + ((int64_t)b * n_q + g * kGroup + hr) * kHeadDim;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const bf16x8*>(qp + 8 * (4 * st + G4));
+  } else {
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qa[st][i] = (__bf16)0.0f;
+  }
+  const int p0 = c * CP;
+  const int tbl = (l < CP && p0 + l < P.pages_per_row) ? P.table[(int64_t)b * P.pages_per_row + p0 + l] : -1;
+  if (pos < 0 || pos >= P.pages_per_row * kPageSize) {
+    // no keys: NaN outputs (as the float32 kernel gives them), written by chunk 0
+    if (c == 0) {
+      float* orow = P.out + ((int64_t)b * n_q + g * kGroup) * kHeadDim;
+      for (int e = tid; e < kGroup * kHeadDim; e += 256) orow[e] = __builtin_nanf("");
+    }
+    return;
+  }
+  const int np = pos / kPageSize + 1;
+  if (p0 >= np) return;
+  const int n_pg = min(np - p0, CP);       // pages of this chunk
+  const int nc = (np + CP - 1) / CP;       // chunks of the row
+
+  // ---- all the chunk's pages in flight
+  PageRegs r[CP];
+#pragma unroll
+  for (int i = 0; i < CP; ++i) {
+    r[i].ok = false;
+    if (i < n_pg) {
+      const int64_t page = __builtin_amdgcn_readlane(tbl, i);
+      r[i].ok = page >= 0 && page < P.num_pages;
+      const int64_t pg = r[i].ok ? page : 0;
+      const uint16_t* krow = P.k_pool + ((int64_t)g * pool_slots + pg * kPageSize + 16 * w + hr) * kHeadDim + 8 * G4;
+      const uint16_t* vrow =
+          P.v_pool + ((int64_t)g * pool_slots + pg * kPageSize + 16 * w + 4 * G4) * kHeadDim + 8 * hr;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + 32 * st));
+        r[i].k[st] = __builtin_bit_cast(bf16x8, x);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vrow + jj * kHeadDim));
+        r[i].v[jj] = make_uint4(x[0], x[1], x[2], x[3]);
+      }
+    }
+  }
+
+  // ---- per page: scores (MFMA), online softmax per head, P.V
+  float m[kGroup], lsum[kGroup], acc[kGroup][8];
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) {
+    m[i] = -INFINITY;
+    lsum[i] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[i][d] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < CP; ++i) {
+    if (i >= n_pg) break;
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], r[i].k[st], sc, 0, 0, 0);
+    const int key0 = (p0 + i) * kPageSize + 16 * w;
+    const bool kvalid = r[i].ok && key0 + hr <= pos;
+    float pr[kGroup], corr[kGroup];
+    bool any_change = false;
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+      const float x = kvalid ? sc[h] * P.scale_log2 : -INFINITY;
+      const float pm = lane0(row_max16(x));
+      const float mn = fmaxf(m[h], pm);
+      corr[h] = (m[h] == mn) ? 1.f : __builtin_amdgcn_exp2f(m[h] - mn);
+      any_change |= (m[h] != mn);
+      const float ms = (mn == -INFINITY) ? 0.f : mn;
+      pr[h] = __builtin_amdgcn_exp2f(x - ms);
+      lsum[h] = lsum[h] * corr[h] + pr[h];
+      m[h] = mn;
+    }
+    if (l < 16) *reinterpret_cast<float4*>(&s_p[w][l][0]) = make_float4(pr[0], pr[1], pr[2], pr[3]);
+    __builtin_amdgcn_wave_barrier();
+    if (any_change) {
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[h][d] *= corr[h];
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int kk = 4 * G4 + jj;
+      const bool vok = r[i].ok && key0 + kk <= pos;
+      const float4 ph = *reinterpret_cast<const float4*>(&s_p[w][kk][0]);
+      float vf[8];
+      vf[0] = bf16_lo(r[i].v[jj].x); vf[1] = bf16_hi(r[i].v[jj].x);
+      vf[2] = bf16_lo(r[i].v[jj].y); vf[3] = bf16_hi(r[i].v[jj].y);
+      vf[4] = bf16_lo(r[i].v[jj].z); vf[5] = bf16_hi(r[i].v[jj].z);
+      vf[6] = bf16_lo(r[i].v[jj].w); vf[7] = bf16_hi(r[i].v[jj].w);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const float x = vok ? vf[d] : 0.f;
+        acc[0][d] += ph.x * x;
+        acc[1][d] += ph.y * x;
+        acc[2][d] += ph.z * x;
+        acc[3][d] += ph.w * x;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- the four waves' states merged through LDS
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h) {
+    lsum[h] = row_sum16(lsum[h]);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[h][d] = group_sum4(acc[h][d]);
+  }
+  if (l < 16) {
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+      float4* dst = reinterpret_cast<float4*>(&s_acc[w][h][8 * l]);
+      dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+  }
+  if (l == 0) {
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) { s_m[w][h] = m[h]; s_l[w][h] = lsum[h]; }
+  }
+  __syncthreads();
+  const int hi = tid / TPH;
+  const int dd = DPT * (tid % TPH);
+  float M = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_m[ww][hi]);
+  float L = 0.f, A[DPT];
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) A[e] = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    const float mw = s_m[ww][hi];
+    const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+    L += f * s_l[ww][hi];
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) A[e] += f * s_acc[ww][hi][dd + e];
+  }
+  float* orow = P.out + ((int64_t)b * n_q + g * kGroup + hi) * kHeadDim + dd;
+  float gt[DPT] = {1.f, 1.f};
+  if (P.gate) {   // output gate: out *= sigmoid(gate) at the same element
+    const uint32_t gw =
+        *reinterpret_cast<const uint32_t*>(P.gate + ((int64_t)b * n_q + g * kGroup + hi) * kHeadDim + dd);
+    gt[0] = sigmoidf(bf16_lo(gw));
+    gt[1] = sigmoidf(bf16_hi(gw));
+  }
+  if (nc == 1) {
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) orow[e] = (A[e] / L) * gt[e];
+    return;
+  }
+  // ---- partial state of chunk c; the last chunk of the row to finish merges them
+  float* part = P.partials + ((int64_t)bg * C + c) * kPartial + hi * (kHeadDim + 2);
+  if ((tid % TPH) == 0) { store_sc1(part, M); store_sc1(part + 1, L); }
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) store_sc1(part + 2 + dd + e, A[e]);
+  __builtin_amdgcn_s_waitcnt(0);   // the partial is at the coherence point before the ticket
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(&P.counters[bg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old == nc - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  float Mx = -INFINITY, Lt = 0.f, B[DPT] = {0.f, 0.f};
+  for (int c0 = 0; c0 < nc; c0 += 8) {
+    float mv[8], lv[8], x[8][DPT];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool ok = c0 + k < nc;
+      const float* ps = P.partials + ((int64_t)bg * C + (ok ? c0 + k : 0)) * kPartial + hi * (kHeadDim + 2);
+      mv[k] = ok ? load_sc1(ps) : -INFINITY;
+      lv[k] = ok ? load_sc1(ps + 1) : 0.f;
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) x[k][e] = ok ? load_sc1(ps + 2 + dd + e) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (mv[k] == -INFINITY) continue;
+      const float mn = fmaxf(Mx, mv[k]);
+      const float fo = (Mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mx - mn);
+      const float fi = __builtin_amdgcn_exp2f(mv[k] - mn);
+      Lt = Lt * fo + lv[k] * fi;
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) B[e] = B[e] * fo + x[k][e] * fi;
+      Mx = mn;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) orow[e] = (B[e] / Lt) * gt[e];
+  if (tid == 0) __hip_atomic_store(&P.counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kChunkPages = 2;
+
+__global__ __launch_bounds__(256) void paged_decode_small_kernel(DecodeParams P, int chunks_per_row) {
+  decode_chunk<kChunkPages>(P, blockIdx.x, chunks_per_row, threadIdx.x);
+}
+
 int grid_for_device() {
   static int cached[64] = {0};
   int dev = 0;
@@ -134,7 +372,17 @@ hipError_t launch_decode_bf16(hipStream_t stream, const AttnArgs& a) {
   // rows x KV heads x pages per row on the units; two rounds from 300 units per
   // resident workgroup.
   int grid = grid_for_device();
-  if ((int64_t)a.n_queries * a.n_kv_heads * a.pages_per_row >= 300LL * grid) grid = std::min(kMaxGrid, 2 * grid);
+  // Small batches: the fixed (row, KV head, chunk) grid, when the bound rows x KV
+  // heads x pages per row is at most 16 pages per resident workgroup and the
+  // chunks' partial states fit the workspace's partial area.
+  const int64_t bound_units = (int64_t)a.n_queries * a.n_kv_heads * a.pages_per_row;
+  const int chunks = (a.pages_per_row + kChunkPages - 1) / kChunkPages;
+  const int64_t small_grid = (int64_t)a.n_queries * a.n_kv_heads * chunks;
+  if (bound_units <= 16LL * grid && small_grid <= 2LL * kMaxGrid) {
+    hipLaunchKernelGGL(paged_decode_small_kernel, dim3((unsigned)small_grid), dim3(256), 0, stream, P, chunks);
+    return hipGetLastError();
+  }
+  if (bound_units >= 300LL * grid) grid = std::min(kMaxGrid, 2 * grid);
   const size_t lds = (size_t)(a.n_queries + 1) * sizeof(int);
   hipLaunchKernelGGL(paged_decode_bf16_kernel, dim3(grid), dim3(256), lds, stream, P);
   return hipGetLastError();
