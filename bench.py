@@ -585,11 +585,24 @@ def main():
             torch.cuda.empty_cache()
     del scratch
 
-    dec_gbs = r["decode"]["gbs"] if step.R else 0.0
+    if step.R:   # the dominant kernel: decode when the step has decode rows, else prefill
+        dec_kernel = Q.decode_kernel_name(step.k_pool, w.n_q_heads, step.R, w.pages_per_row)
+        roofline = {"bound": "hbm", "achieved": r["decode"]["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(r["decode"]["gbs"] / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(dec_kernel, DECODE_SOURCES)
+                    if (args.workload == 4 and args.kv_heads == 8) else None,
+                    "kernel": dec_kernel,
+                    "bytes_per_launch": r["decode"]["bytes_per_launch"],
+                    "ms_per_launch": round(times["decode"], 5)}
+    else:
+        roofline = {"bound": "mfma", "achieved": r["prefill"]["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": r["prefill"]["frac"], "traffic": None,
+                    "kernel": "paged_prefill_bf16_kernel", "flops_per_launch": r["prefill"]["flops_per_launch"],
+                    "ms_per_launch": r["prefill"]["ms_per_launch"]}
     result = {
         "metric": METRIC,
-        "value": round(dec_gbs, 2),
-        "unit": "GB/s",
+        "value": roofline["achieved"],
+        "unit": roofline["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -606,13 +619,7 @@ def main():
                    "pool_pages": w.num_pages, "page_size": 64, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
                    "head_dim": 128,
                    "caches": "MALL and L2 flushed before every step" if flushed else "warm (back to back)"},
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("paged_decode_bf16_kernel", DECODE_SOURCES)
-                     if (args.workload == 4 and args.kv_heads == 8) else None,
-                     "kernel": "paged_decode_bf16_kernel",
-                     "bytes_per_launch": r["decode"]["bytes_per_launch"] if step.R else 0,
-                     "ms_per_launch": round(times["decode"], 5)},
+        "roofline": roofline,
     }
     if step.P:
         result["prefill"] = {**r["prefill"], "peak": MFMA_BF16_PEAK_TFLOPS}

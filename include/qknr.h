@@ -196,6 +196,14 @@ int paged_decode_attn(void* stream, const qkr_pool* pool, int32_t n_rows,
 
 size_t paged_decode_attn_workspace(const qkr_pool* pool, int32_t n_rows, int32_t pages_per_row);
 
+/* The name of the kernel paged_decode_attn launches for n_rows rows and tables of
+ * pages_per_row pages on the current device, as profilers list it:
+ * "paged_decode_small_kernel" (one workgroup per row, KV head and chunk of 2 pages,
+ * for small batches), "paged_decode_bf16_kernel" (the split-K grid) or
+ * "attention_generic_kernel" (a float32 pool). "" for an invalid pool or size.
+ * The string is static; nothing is launched. */
+const char* paged_decode_attn_kernel(const qkr_pool* pool, int32_t n_rows, int32_t pages_per_row);
+
 /* paged_decode_attn with qkr_attn_opts (output gate). */
 int paged_decode_attn_ex(void* stream, const qkr_pool* pool, int32_t n_rows,
                          const void* q, const void* k_pool, const void* v_pool,

@@ -28,6 +28,7 @@ EXPORTED = (
     "paged_decode_attn",
     "paged_decode_attn_ex",
     "paged_decode_attn_workspace",
+    "paged_decode_attn_kernel",
     "paged_decode_attn_noalloc",
     "paged_prefill_attn",
     "paged_prefill_attn_ex",
@@ -112,6 +113,8 @@ def _load():
     lib.paged_decode_attn_noalloc.argtypes = [vp, pool_p, i32, vp, vp, vp, vp, i32, vp, f32, vp]
     lib.paged_decode_attn_workspace.restype = sz
     lib.paged_decode_attn_workspace.argtypes = [pool_p, i32, i32]
+    lib.paged_decode_attn_kernel.restype = ctypes.c_char_p
+    lib.paged_decode_attn_kernel.argtypes = [pool_p, i32, i32]
     lib.paged_prefill_attn.restype = ctypes.c_int
     lib.paged_prefill_attn.argtypes = [vp, pool_p, i32, vp, vp, vp, vp, i32, i32, vp, vp, f32, vp, vp, sz]
     lib.paged_prefill_attn_workspace.restype = sz
@@ -241,6 +244,12 @@ def qknorm_rope_append(q, k, v, q_gain, k_gain, rope_cos, rope_sin, positions, q
 def decode_workspace_bytes(k_pool, num_q_heads: int, n_rows: int, pages_per_row: int) -> int:
     pool = pool_desc(k_pool, num_q_heads)
     return int(LIB.paged_decode_attn_workspace(ctypes.byref(pool), int(n_rows), int(pages_per_row)))
+
+
+def decode_kernel_name(k_pool, num_q_heads: int, n_rows: int, pages_per_row: int) -> str:
+    """The kernel paged_decode_attn launches for this batch on the current device."""
+    pool = pool_desc(k_pool, num_q_heads)
+    return LIB.paged_decode_attn_kernel(ctypes.byref(pool), int(n_rows), int(pages_per_row)).decode()
 
 
 def prefill_workspace_bytes(k_pool, num_q_heads: int, n_tokens: int) -> int:

@@ -201,6 +201,13 @@ size_t paged_decode_attn_workspace(const qkr_pool* pool, int32_t n_rows, int32_t
   return qknr::decode_workspace_bytes(n_rows, pool->num_kv_heads, pages_per_row);
 }
 
+const char* paged_decode_attn_kernel(const qkr_pool* pool, int32_t n_rows, int32_t pages_per_row) {
+  if (check_pool(pool) != QKR_OK || n_rows <= 0 || pages_per_row <= 0) return "";
+  if (pool->dtype != QKR_BF16) return "attention_generic_kernel";
+  return qknr::decode_uses_small_kernel(n_rows, pool->num_kv_heads, pages_per_row) ? "paged_decode_small_kernel"
+                                                                                   : "paged_decode_bf16_kernel";
+}
+
 int paged_decode_attn_ex(void* stream, const qkr_pool* pool, int32_t n_rows,
                          const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* table, int32_t pages_per_row,

@@ -344,6 +344,16 @@ size_t decode_workspace_bytes(int n_rows, int n_kv_heads, int /*pages_per_row*/)
 
 int decode_max_rows() { return kMaxRows; }
 
+// Small batches take the fixed (row, KV head, chunk) grid: when the bound rows x KV
+// heads x pages per row is at most 16 pages per resident workgroup and the chunks'
+// partial states fit the workspace's partial area.
+bool decode_uses_small_kernel(int n_rows, int n_kv_heads, int pages_per_row) {
+  const int64_t bound_units = (int64_t)n_rows * n_kv_heads * pages_per_row;
+  const int chunks = (pages_per_row + kChunkPages - 1) / kChunkPages;
+  const int64_t small_grid = (int64_t)n_rows * n_kv_heads * chunks;
+  return bound_units <= 16LL * grid_for_device() && small_grid <= 2LL * kMaxGrid;
+}
+
 hipError_t launch_decode_bf16(hipStream_t stream, const AttnArgs& a) {
   const size_t pairs = (size_t)a.n_queries * a.n_kv_heads;
   const size_t counter_bytes = (pairs * sizeof(int) + 255) / 256 * 256;
@@ -372,13 +382,10 @@ hipError_t launch_decode_bf16(hipStream_t stream, const AttnArgs& a) {
   // rows x KV heads x pages per row on the units; two rounds from 300 units per
   // resident workgroup.
   int grid = grid_for_device();
-  // Small batches: the fixed (row, KV head, chunk) grid, when the bound rows x KV
-  // heads x pages per row is at most 16 pages per resident workgroup and the
-  // chunks' partial states fit the workspace's partial area.
   const int64_t bound_units = (int64_t)a.n_queries * a.n_kv_heads * a.pages_per_row;
-  const int chunks = (a.pages_per_row + kChunkPages - 1) / kChunkPages;
-  const int64_t small_grid = (int64_t)a.n_queries * a.n_kv_heads * chunks;
-  if (bound_units <= 16LL * grid && small_grid <= 2LL * kMaxGrid) {
+  if (decode_uses_small_kernel(a.n_queries, a.n_kv_heads, a.pages_per_row)) {
+    const int chunks = (a.pages_per_row + kChunkPages - 1) / kChunkPages;
+    const int64_t small_grid = (int64_t)a.n_queries * a.n_kv_heads * chunks;
     hipLaunchKernelGGL(paged_decode_small_kernel, dim3((unsigned)small_grid), dim3(256), 0, stream, P, chunks);
     return hipGetLastError();
   }

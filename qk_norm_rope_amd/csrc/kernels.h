@@ -51,6 +51,8 @@ int append_max_whole_heads();
 size_t decode_workspace_bytes(int n_rows, int n_kv_heads, int pages_per_row);
 int decode_max_rows();
 hipError_t launch_decode_bf16(hipStream_t stream, const AttnArgs& a);
+// true when launch_decode_bf16 takes the (row, KV head, chunk) kernel on the current device
+bool decode_uses_small_kernel(int n_rows, int n_kv_heads, int pages_per_row);
 // The same kernel on the library's own per-device scratch (no workspace argument,
 // no allocation); rows x KV heads at most decode_noalloc_max_pairs().
 int decode_noalloc_max_pairs();

@@ -167,6 +167,14 @@ def test_workspace_sizes_grow_with_work():
     assert L.LIB.paged_prefill_attn_workspace(ctypes.byref(pool), 4096) >= 64 * 4
 
 
+def test_decode_kernel_name_host_cases():
+    # a float32 pool and invalid sizes need no device; the bfloat16 choice is checked on the GPU
+    assert L.LIB.paged_decode_attn_kernel(ctypes.byref(_pool(dtype=L.QKR_F32)), 8, 65) == b"attention_generic_kernel"
+    assert L.LIB.paged_decode_attn_kernel(ctypes.byref(_pool()), 0, 65) == b""
+    assert L.LIB.paged_decode_attn_kernel(ctypes.byref(_pool()), 8, 0) == b""
+    assert L.LIB.paged_decode_attn_kernel(None, 8, 65) == b""
+
+
 def test_rope_table_rejects_bad_arguments():
     buf = np.zeros(4, np.float32)
     p = buf.ctypes.data_as(ctypes.c_void_p)

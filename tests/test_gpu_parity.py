@@ -295,3 +295,15 @@ def test_decode_many_short_segments_per_workgroup():
     kp, vp = oracle_pools(w, k_rows, v_rows, slots)
     ref = O.decode(ref_q, w.dtype, kp, vp, w.dtype, w.decode_table, w.step_positions, W.SCALE)
     report("many short segments", run.dec_out.cpu().numpy(), ref, TOL_BF16)
+
+
+def test_decode_kernel_choice_on_the_standard_workloads():
+    # 8 rows take the (row, KV head, 2-page chunk) kernel, 64 and 128 rows the split-K grid
+    import qk_norm_rope_amd as Q
+    names = {}
+    for cfg in (1, 2, 4):
+        w = W.config(cfg)
+        pool = torch.empty((w.n_kv_heads, 64, 128), dtype=torch.bfloat16, device=DEV)
+        names[cfg] = Q.decode_kernel_name(pool, w.n_q_heads, w.n_decode, w.pages_per_row)
+    print(f"[parity] decode kernels: {names}", flush=True)
+    assert names == {1: "paged_decode_small_kernel", 2: "paged_decode_bf16_kernel", 4: "paged_decode_bf16_kernel"}
