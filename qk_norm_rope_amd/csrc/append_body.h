@@ -26,22 +26,27 @@ namespace {
 
 template <typename T> struct Vec8;
 template <> struct Vec8<float> {
-  __device__ static void load(const float* p, float (&o)[8]) {
-    const float4 u = *reinterpret_cast<const float4*>(p);
-    const float4 v = *reinterpret_cast<const float4*>(p + 4);
-    o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w; o[4] = v.x; o[5] = v.y; o[6] = v.z; o[7] = v.w;
+  struct Raw { float4 u, v; };
+  __device__ static Raw load_raw(const float* p) {
+    return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
   }
+  __device__ static void unpack(const Raw& r, float (&o)[8]) {
+    o[0] = r.u.x; o[1] = r.u.y; o[2] = r.u.z; o[3] = r.u.w; o[4] = r.v.x; o[5] = r.v.y; o[6] = r.v.z; o[7] = r.v.w;
+  }
+  __device__ static void load(const float* p, float (&o)[8]) { unpack(load_raw(p), o); }
   __device__ static void store(float* p, const float (&o)[8]) {
     *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
     *reinterpret_cast<float4*>(p + 4) = make_float4(o[4], o[5], o[6], o[7]);
   }
 };
 template <> struct Vec8<uint16_t> {
-  __device__ static void load(const uint16_t* p, float (&o)[8]) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+  typedef uint4 Raw;
+  __device__ static Raw load_raw(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void unpack(const Raw& v, float (&o)[8]) {
     o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
     o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
   }
+  __device__ static void load(const uint16_t* p, float (&o)[8]) { unpack(load_raw(p), o); }
   __device__ static void store(uint16_t* p, const float (&o)[8]) {
     uint4 v;
     v.x = f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16);
@@ -97,14 +102,38 @@ __device__ __forceinline__ void append_token(
   __shared__ float s_ss[WHOLE ? 2 : 1][WHOLE ? kMaxWholeHeads : 1];
   __shared__ float s_r[2];
   __shared__ float s_y[PARTIAL ? 32 : 1][PARTIAL ? kHeadDim : 1];
+  typedef Vec8<TIn> VIn;
+  typedef typename VIn::Raw RawIn;
+  const int j = tid & 7;     // lane within the head vector's 8
+  const int grp = tid >> 3;  // 32 head vectors in flight
+  const int n_norm = n_q_heads + n_kv_heads;
+  const int n_v8 = n_kv_heads * (kHeadDim / 8);   // 8-element pieces of the token's v
+  auto source = [&](int hv) -> const TIn* {
+    return hv < n_q_heads ? q + ((int64_t)t * n_q_heads + hv) * kHeadDim
+                          : k + ((int64_t)t * n_kv_heads + (hv - n_q_heads)) * kHeadDim;
+  };
+
+  // Every load the position does not decide goes out with the position's: the
+  // first two head vectors of the lane's group (hv = grp, grp + 32), its first
+  // piece of v and a caller-given slot. Only the page table and the rotation's
+  // cos/sin wait for the position.
   const int pos = t < n_first ? positions[t] : positions2[t - n_first];
+  RawIn ra[2] = {}, rb[2] = {}, rv = {};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int hv = grp + 32 * u;
+    if (hv < n_norm) {
+      ra[u] = VIn::load_raw(source(hv) + 8 * j);
+      rb[u] = VIn::load_raw(source(hv) + kHeadDim / 2 + 8 * j);
+    }
+  }
+  if (tid < n_v8) rv = VIn::load_raw(v + (int64_t)t * n_kv_heads * kHeadDim + 8 * tid);
+  int64_t slot = -1;
+  if (t < n_slotted) slot = slots[t];
   if (pos < 0 || pos >= rope_rows) return;  // no rotation exists for it: skip the token
 
   const int64_t pool_slots = num_pages * kPageSize;
-  int64_t slot = -1;
-  if (t < n_slotted) {
-    slot = slots[t];
-  } else {
+  if (t >= n_slotted) {
     const int b = t - n_slotted;
     const int pg = pos / kPageSize;
     if (pg < pages_per_row) {
@@ -114,8 +143,6 @@ __device__ __forceinline__ void append_token(
   }
   if (slot >= pool_slots) slot = -1;
 
-  const int j = tid & 7;     // lane within the head vector's 8
-  const int grp = tid >> 3;  // 32 head vectors in flight
   const int half_r = PARTIAL ? rotary_dim / 2 : kHeadDim / 2;
   float c[8], s[8];
   if (!PARTIAL) {
@@ -137,11 +164,6 @@ __device__ __forceinline__ void append_token(
     }
   }
 
-  const int n_norm = n_q_heads + n_kv_heads;
-  auto source = [&](int hv) -> const TIn* {
-    return hv < n_q_heads ? q + ((int64_t)t * n_q_heads + hv) * kHeadDim
-                          : k + ((int64_t)t * n_kv_heads + (hv - n_q_heads)) * kHeadDim;
-  };
   // per-head sum of squares: lane j holds elements 8j..8j+7 of each half; its
   // in-lane adds are the first three levels of the pairwise tree over the 64
   // p_i, the three xor-shuffles the rest
@@ -156,11 +178,26 @@ __device__ __forceinline__ void append_token(
     return ss;
   };
 
+  // the two halves of head vector hv (iteration (hv - grp) / 32 of the group):
+  // the first two iterations' were loaded at the start
+  auto fetch = [&](int hv, float (&a)[8], float (&b)[8]) {
+    const int it = (hv - grp) >> 5;
+    if (it == 0) {
+      VIn::unpack(ra[0], a);
+      VIn::unpack(rb[0], b);
+    } else if (it == 1) {
+      VIn::unpack(ra[1], a);
+      VIn::unpack(rb[1], b);
+    } else {
+      VIn::load(source(hv) + 8 * j, a);
+      VIn::load(source(hv) + kHeadDim / 2 + 8 * j, b);
+    }
+  };
+
   if (WHOLE) {
     for (int hv = grp; hv < n_norm; hv += 32) {
       float a[8], b[8];
-      Vec8<TIn>::load(source(hv) + 8 * j, a);
-      Vec8<TIn>::load(source(hv) + kHeadDim / 2 + 8 * j, b);
+      fetch(hv, a, b);
       const float ss = head_ss(a, b);
       if (j == 0) {
         if (hv < n_q_heads) s_ss[0][hv] = ss;
@@ -181,7 +218,6 @@ __device__ __forceinline__ void append_token(
   }
 
   for (int hv = grp; hv < n_norm; hv += 32) {
-    const TIn* src = source(hv);
     const float* g;
     TOut* dst;
     bool write = true;
@@ -198,8 +234,7 @@ __device__ __forceinline__ void append_token(
     }
     if (WHOLE) g += (int64_t)hl * kHeadDim;
     float a[8], b[8];
-    Vec8<TIn>::load(src + 8 * j, a);
-    Vec8<TIn>::load(src + kHeadDim / 2 + 8 * j, b);
+    fetch(hv, a, b);
 
     float r;
     if (WHOLE) {
@@ -270,12 +305,13 @@ __device__ __forceinline__ void append_token(
   }
 
   if (slot >= 0) {
-    // v: cast only, 8 elements per thread per pass
-    for (int e = tid; e < n_kv_heads * (kHeadDim / 8); e += 256) {
+    // v: cast only, 8 elements per thread per pass (the first pass loaded at the start)
+    for (int e = tid; e < n_v8; e += 256) {
       const int kh = e / (kHeadDim / 8);
       const int c8 = e % (kHeadDim / 8);
       float x[8];
-      Vec8<TIn>::load(v + ((int64_t)t * n_kv_heads + kh) * kHeadDim + 8 * c8, x);
+      if (e == tid) VIn::unpack(rv, x);
+      else VIn::load(v + ((int64_t)t * n_kv_heads + kh) * kHeadDim + 8 * c8, x);
       Vec8<TOut>::store(v_pool + ((int64_t)kh * pool_slots + slot) * kHeadDim + 8 * c8, x);
     }
   }
