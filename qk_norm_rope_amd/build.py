@@ -29,7 +29,9 @@ SOURCES = {
     # The append kernel's float32 arithmetic must not be contracted into FMAs:
     # its stored bytes are specified operation by operation.
     "append.hip": ["-ffp-contract=off"],
-    "decode.hip": [],
+    # MFMA accumulators in VGPRs: the small-batch decode kernel otherwise takes 4
+    # AGPRs on top of 126 VGPRs, which leaves room for 3 workgroups per CU instead of 4
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
     "prefill.hip": [],
     "generic.hip": [],
     "step.hip": [],
