@@ -238,6 +238,39 @@ def measure_fused(step, stream, steps, scratch):
     return {"ms_per_step": round(ms, 4), "kernel": "step_paged_kernel", "launches": 1, "wait_gave_up": fault}
 
 
+def measure_hbm_reference(Q, dev, reps=5):
+    """What plain streaming kernels reach on this GPU: the library's read probe (a
+    grid-stride read, no paging, masking or attention arithmetic) over 4 GiB, and
+    torch's copy_ (a read and a write) over 1 GiB, both far beyond the 256 MB MALL.
+    The roofline peak stays the published 8 TB/s; these say how much of it the
+    simplest kernels get on the same GPU."""
+    import torch
+    big = torch.ones(4 * COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    x = big[:COPY_PROBE_BYTES // 4]
+    y = torch.empty_like(x)
+    for _ in range(2):
+        Q.read_probe(big, sink)
+        y.copy_(x)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        Q.read_probe(big, sink)
+    ev[1].record()
+    for _ in range(reps):
+        y.copy_(x)
+    ev[2].record()
+    torch.cuda.synchronize()
+    read_ms = ev[0].elapsed_time(ev[1]) / reps
+    copy_ms = ev[1].elapsed_time(ev[2]) / reps
+    del big, x, y, sink
+    torch.cuda.empty_cache()
+    return {"read_gbs": round(4 * COPY_PROBE_BYTES / (read_ms * 1e-3) / 1e9, 1),
+            "copy_gbs": round(2 * COPY_PROBE_BYTES / (copy_ms * 1e-3) / 1e9, 1),
+            "source": "qkr_read_probe over 4 GiB (read); torch copy_ over 1 GiB (read + write); HIP events"}
+
+
 def measure_append_steady(step, stream, reps=50):
     """The step's append, launched back to back (its in-step event window also holds
     the launch gap after the previous step's last kernel)."""
@@ -573,6 +606,7 @@ def main():
     app_steady_ms = measure_append_steady(step, stream) if extras else None
     packed = measure_packed(step, stream) if (step.P and extras) else None
     variants = measure_variants(step, stream) if extras else None
+    hbm_ref = measure_hbm_reference(Q, dev) if extras else None
     others = None
     if extras and args.workload == 4 and args.kv_heads == 8:
         others = {}
@@ -642,6 +676,10 @@ def main():
         result["packed_prefill"] = packed
     if variants is not None:
         result["variants"] = variants
+    if hbm_ref is not None:
+        if roofline["unit"] == "GB/s":
+            hbm_ref["decode_frac_of_read"] = round(roofline["achieved"] / hbm_ref["read_gbs"], 4)
+        result["hbm_reference"] = hbm_ref
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, snap)
     print(json.dumps(result), flush=True)

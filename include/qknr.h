@@ -413,6 +413,18 @@ int qkr_check_indices(void* stream, const qkr_pool* pool,
 int qkr_rope_table(double theta, int32_t rope_rows, int32_t head_dim,
                    float* cos_out, float* sin_out);
 
+/*
+ * qkr_read_probe -- measurement helper, not part of the attention path: one plain
+ * streaming read of `bytes` bytes of device memory at `buf` (16-byte aligned,
+ * bytes a multiple of 16), enqueued on `stream`. Timing it gives the read rate a
+ * kernel with no paging, masking or attention arithmetic reaches on this GPU, a
+ * practical ceiling to set beside the published HBM peak. `out` (device, 1 float)
+ * is written only in the practically impossible case that the buffer sums to a
+ * fixed sentinel; its content is not meaningful. Returns QKR_EINVAL for a null
+ * pointer, a misaligned buffer or a size that is not a multiple of 16.
+ */
+int qkr_read_probe(void* stream, const void* buf, size_t bytes, float* out);
+
 /* Human-readable name of a qkr_status value. */
 const char* qkr_status_str(int status);
 

@@ -39,6 +39,7 @@ EXPORTED = (
     "step_paged",
     "step_paged_workspace",
     "qkr_check_indices",
+    "qkr_read_probe",
     "qkr_rope_table",
     "qkr_status_str",
     "qkr_last_error",
@@ -136,6 +137,8 @@ def _load():
     lib.qkr_status_str.argtypes = [ctypes.c_int]
     lib.qkr_last_error.restype = ctypes.c_char_p
     lib.qkr_last_error.argtypes = []
+    lib.qkr_read_probe.restype = ctypes.c_int
+    lib.qkr_read_probe.argtypes = [vp, vp, sz, vp]
     lib.qkr_version.restype = ctypes.c_int
     lib.qkr_version.argtypes = []
     return lib
@@ -410,6 +413,20 @@ def check_indices(k_pool, num_q_heads: int, table, rows=None, positions=None, sl
         return st, counts
     c = counts.cpu().tolist()
     return st, {name: int(c[i]) for i, name in enumerate(CHECK_NAMES)}
+
+
+def read_probe(buf, out, stream=None) -> None:
+    """qkr_read_probe: one plain streaming read of the device tensor buf (a
+    measurement helper, not part of the attention path); out: 1 float32 on the
+    same device."""
+    import torch
+    if not buf.is_cuda or not out.is_cuda or out.dtype != torch.float32 or out.numel() < 1:
+        raise ValueError("read_probe needs a device buffer and one device float32")
+    if not buf.is_contiguous():
+        raise ValueError("read_probe needs a contiguous buffer")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    _check(LIB.qkr_read_probe(ctypes.c_void_p(s.cuda_stream), ctypes.c_void_p(buf.data_ptr()),
+                              buf.numel() * buf.element_size(), ctypes.c_void_p(out.data_ptr())), "qkr_read_probe")
 
 
 def version() -> int:

@@ -36,6 +36,7 @@ SOURCES = {
     "generic.hip": [],
     "step.hip": [],
     "check.hip": [],
+    "probe.hip": [],
     "api.cpp": ["-ffp-contract=off"],
 }
 

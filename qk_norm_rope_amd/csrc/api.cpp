@@ -102,6 +102,12 @@ extern "C" {
 
 int qkr_version(void) { return 100; }
 
+int qkr_read_probe(void* stream, const void* buf, size_t bytes, float* out) {
+  if (!buf || !out || (reinterpret_cast<uintptr_t>(buf) & 15) != 0 || bytes % 16 != 0) return QKR_EINVAL;
+  if (bytes == 0) return QKR_OK;
+  return launch_status(qknr::launch_read_probe(static_cast<hipStream_t>(stream), buf, bytes, out));
+}
+
 const char* qkr_last_error(void) { return g_last_error; }
 
 const char* qkr_status_str(int s) {

@@ -109,6 +109,9 @@ struct CheckArgs {
   int rope_rows;   // 0: no rotation-table limit
   int32_t* counts;
 };
+// plain streaming read of bytes (a multiple of 16) at buf, 16-byte aligned
+hipError_t launch_read_probe(hipStream_t stream, const void* buf, size_t bytes, float* out);
+
 hipError_t launch_check_indices(hipStream_t stream, const CheckArgs& a);
 
 size_t step_workspace_bytes(int n_prefill, int n_decode, int n_kv_heads, int pages_per_row);

@@ -175,6 +175,15 @@ def test_decode_kernel_name_host_cases():
     assert L.LIB.paged_decode_attn_kernel(None, 8, 65) == b""
 
 
+def test_read_probe_host_checks():
+    lib = L.LIB
+    assert lib.qkr_read_probe(None, None, 16, ctypes.c_void_p(0x1000)) == -1            # null buffer
+    assert lib.qkr_read_probe(None, ctypes.c_void_p(0x1008), 16, ctypes.c_void_p(0x1000)) == -1   # misaligned
+    assert lib.qkr_read_probe(None, ctypes.c_void_p(0x1000), 15, ctypes.c_void_p(0x1000)) == -1   # size
+    assert lib.qkr_read_probe(None, ctypes.c_void_p(0x1000), 16, None) == -1            # null out
+    assert lib.qkr_read_probe(None, ctypes.c_void_p(0x1000), 0, ctypes.c_void_p(0x1000)) == 0     # nothing to read
+
+
 def test_rope_table_rejects_bad_arguments():
     buf = np.zeros(4, np.float32)
     p = buf.ctypes.data_as(ctypes.c_void_p)

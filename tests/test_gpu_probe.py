@@ -1,0 +1,18 @@
+"""qkr_read_probe (a measurement helper outside the attention path) through the C
+ABI: it reads the buffer and leaves the output alone."""
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+def test_read_probe_reads_and_writes_nothing():
+    import qk_norm_rope_amd as Q
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    buf = torch.ones(3 * 1024 * 1024 + 4, dtype=torch.float32, device="cuda")   # not a multiple of the grid's step
+    out = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+    Q.read_probe(buf, out)
+    torch.cuda.synchronize()
+    assert float(out) == 7.0
+    with pytest.raises(Q.QknrError):
+        Q.read_probe(buf[1:], out)   # 4-byte offset: misaligned
