@@ -34,6 +34,10 @@ template <> struct Vec8<float> {
     o[0] = r.u.x; o[1] = r.u.y; o[2] = r.u.z; o[3] = r.u.w; o[4] = r.v.x; o[5] = r.v.y; o[6] = r.v.z; o[7] = r.v.w;
   }
   __device__ static void load(const float* p, float (&o)[8]) { unpack(load_raw(p), o); }
+  __device__ static void store_agent(float* p, const float (&o)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) __hip_atomic_store(p + i, o[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __device__ static void store(float* p, const float (&o)[8]) {
     *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
     *reinterpret_cast<float4*>(p + 4) = make_float4(o[4], o[5], o[6], o[7]);
@@ -47,6 +51,15 @@ template <> struct Vec8<uint16_t> {
     o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
   }
   __device__ static void load(const uint16_t* p, float (&o)[8]) { unpack(load_raw(p), o); }
+  __device__ static void store_agent(uint16_t* p, const float (&o)[8]) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+    const uint64_t a = (uint64_t)(f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16)) |
+                       ((uint64_t)(f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16)) << 32);
+    const uint64_t b = (uint64_t)(f32_to_bf16(o[4]) | (f32_to_bf16(o[5]) << 16)) |
+                       ((uint64_t)(f32_to_bf16(o[6]) | (f32_to_bf16(o[7]) << 16)) << 32);
+    __hip_atomic_store(q, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __device__ static void store(uint16_t* p, const float (&o)[8]) {
     uint4 v;
     v.x = f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16);
@@ -84,10 +97,13 @@ constexpr int kMaxWholeHeads = 256;   // q heads + kv heads for the whole-vector
 
 // WHOLE: one RMS norm over all heads of q and over all heads of k (gains of width
 // heads*head_dim). PARTIAL: only the first rotary_dim elements of a head rotate.
+// AGENT: every store is an agent-scope relaxed atomic store (written through to
+// the level all XCDs share), for readers in other workgroups of the same launch
+// that synchronise without a cache write-back.
 // Token t by 256 threads (tid 0..255). Positions: token t < n_first reads
 // positions[t], a later one positions2[t - n_first]. WHOLE uses workgroup barriers
 // (the workgroup is the 256 threads).
-template <typename TIn, typename TOut, bool WHOLE, bool PARTIAL>
+template <typename TIn, typename TOut, bool WHOLE, bool PARTIAL, bool AGENT = false>
 __device__ __forceinline__ void append_token(
     const int t, const int tid, int n_q_heads, int n_kv_heads,
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
@@ -299,8 +315,13 @@ __device__ __forceinline__ void append_token(
       __builtin_amdgcn_wave_barrier();   // the row is rewritten by the group's next head
     }
     if (write) {
-      Vec8<TOut>::store(dst + 8 * j, oa);
-      Vec8<TOut>::store(dst + kHeadDim / 2 + 8 * j, ob);
+      if (AGENT) {
+        Vec8<TOut>::store_agent(dst + 8 * j, oa);
+        Vec8<TOut>::store_agent(dst + kHeadDim / 2 + 8 * j, ob);
+      } else {
+        Vec8<TOut>::store(dst + 8 * j, oa);
+        Vec8<TOut>::store(dst + kHeadDim / 2 + 8 * j, ob);
+      }
     }
   }
 
@@ -312,7 +333,9 @@ __device__ __forceinline__ void append_token(
       float x[8];
       if (e == tid) VIn::unpack(rv, x);
       else VIn::load(v + ((int64_t)t * n_kv_heads + kh) * kHeadDim + 8 * c8, x);
-      Vec8<TOut>::store(v_pool + ((int64_t)kh * pool_slots + slot) * kHeadDim + 8 * c8, x);
+      TOut* vd = v_pool + ((int64_t)kh * pool_slots + slot) * kHeadDim + 8 * c8;
+      if (AGENT) Vec8<TOut>::store_agent(vd, x);
+      else Vec8<TOut>::store(vd, x);
     }
   }
 }

@@ -45,6 +45,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // ---------------------------------------------------------------- planning
 // Tile order by decreasing cost, sorted in LDS (keys: at least n_tiles rounded up
 // to a power of two entries) by the nthreads threads of one workgroup.
+template <bool kAgentStores = false>
 __device__ __forceinline__ void plan_tiles(int n_tokens, const int* __restrict__ positions,
                                            const int* __restrict__ lo, int n_tiles, int* __restrict__ order,
                                            unsigned long long* keys, int tid, int nthreads) {
@@ -99,7 +100,11 @@ __device__ __forceinline__ void plan_tiles(int n_tokens, const int* __restrict__
       __syncthreads();
     }
   }
-  for (int i = tid; i < n_tiles; i += nthreads) order[i] = (int)(keys[i] & 0xffffffffu);
+  for (int i = tid; i < n_tiles; i += nthreads) {
+    const int v = (int)(keys[i] & 0xffffffffu);
+    if (kAgentStores) __hip_atomic_store(&order[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else order[i] = v;
+  }
 }
 
 // ---------------------------------------------------------------- attention

@@ -8,11 +8,16 @@
 // cost) and the append chunks (16 tokens each, one token per 256-thread half);
 // after every phase-1 item has published, phase 2 takes prefill work items in plan
 // order, then decode slices, so the two kernels' tails overlap.
-// Visibility across XCDs (each has its own L2): every wave drains its stores, the
-// workgroup meets at a barrier, and one agent-scope release add publishes the
-// item; the wait ends with an agent-scope acquire. The wait polls with relaxed
-// loads (an acquire on every poll would invalidate the XCD's L2 each time, for
-// every waiting workgroup) and is bounded in wall-clock time.
+// Visibility across XCDs (each has its own L2): the phase-1 items write with
+// agent-scope relaxed atomic stores (written through to the level every XCD
+// reads), every wave drains them (s_waitcnt), the workgroup meets at a barrier,
+// and one relaxed add publishes the item; the wait ends with an agent-scope
+// acquire (an L2 invalidate, once per workgroup), so phase 2's plain loads miss
+// any stale copy. A release add per item would write back the XCD's whole L2
+// each time: with 264 append items that alone took about 250 us of the step.
+// The wait polls with relaxed loads (an acquire on every poll would invalidate
+// the XCD's L2 each time, for every waiting workgroup) and is bounded in
+// wall-clock time.
 #include <algorithm>
 
 #include "decode_body.h"
@@ -83,10 +88,12 @@ struct DeviceEnv {
   }
 
   __device__ void publish(int word) {
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's stores are complete
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's agent-coherent stores are complete
     __syncthreads();                 // ... and every other wave's
-    if (wave0)
-      __hip_atomic_fetch_add(&ctl[word], lane == 0 ? 1 : 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (wave0) {
+      const int at = word == kAppendDone ? kShardBase + kShardStride * (int)(blockIdx.x % kAppendShards) : word;
+      __hip_atomic_fetch_add(&ctl[at], lane == 0 ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
   __device__ bool wait_ready(int n_append, int n_plan) {
@@ -95,8 +102,11 @@ struct DeviceEnv {
       const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + kWaitTicks;
       int seen_a = 0, seen_p = 0;
       for (;;) {
-        seen_a = __builtin_amdgcn_readfirstlane(
-            __hip_atomic_load(&ctl[kAppendDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        seen_a = 0;
+#pragma unroll
+        for (int k = 0; k < kAppendShards; ++k)
+          seen_a += __builtin_amdgcn_readfirstlane(__hip_atomic_load(&ctl[kShardBase + kShardStride * k],
+                                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         seen_p = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(&ctl[kPlanDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         if (seen_a >= n_append && seen_p >= n_plan) {
@@ -119,18 +129,22 @@ struct DeviceEnv {
   __device__ int leave() {
     int old = 0;
     if (wave0)
+      // relaxed: the words the last one clears are only touched by atomics, every
+      // one of which a leaving workgroup has completed (its results were used)
       old = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(&ctl[kExited], lane == 0 ? 1 : 0,
-                                                                  __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT));
+                                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     return broadcast_from_wave0(old);
   }
 
   __device__ void clear() {
     if (wave0 && lane < kFault) __hip_atomic_store(&ctl[lane], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wave0 && lane < kAppendShards)
+      __hip_atomic_store(&ctl[kShardBase + kShardStride * lane], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   __device__ void plan() {
     if (S.order)
-      plan_tiles(S.n_prefill, S.positions, nullptr, S.n_tiles, S.order,
+      plan_tiles<true>(S.n_prefill, S.positions, nullptr, S.n_tiles, S.order,
                  reinterpret_cast<unsigned long long*>(sTab), tid, kStepThreads);
   }
 
@@ -139,7 +153,7 @@ struct DeviceEnv {
     for (int i = tid >> 8; i < kAppendPerItem; i += 2) {
       const int t = t0 + i;
       if (t >= S.n_tokens) break;
-      append_token<uint16_t, uint16_t, false, false>(
+      append_token<uint16_t, uint16_t, false, false, true>(
           t, tid & 255, S.n_q_heads, S.n_kv_heads, S.q, S.k, S.v, S.q_gain, S.k_gain, S.eps, S.rope_cos,
           S.rope_sin, S.rope_rows, kHeadDim, S.positions, S.step_positions, S.n_prefill, S.slots,
           S.n_prefill, S.decode_table, S.pages_per_row, S.num_pages, S.q_out, S.k_pool, S.v_pool);

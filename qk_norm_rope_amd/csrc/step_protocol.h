@@ -10,7 +10,8 @@
 // Each workgroup of the persistent grid:
 //   phase 1  takes tickets from word kTicketA: ticket 0 is the tile plan, ticket
 //            i >= 1 the append of chunk i - 1; after each item it publishes (word
-//            kPlanDone or kAppendDone) with a release. No phase-1 item waits for
+//            kPlanDone or kAppendDone) once its writes are where every reader
+//            sees them. No phase-1 item waits for
 //            anything, and every ticket is taken by a running workgroup, so every
 //            phase-1 item completes whatever the number of resident workgroups.
 //   wait     until all append chunks and the plan have published (bounded; an
@@ -19,15 +20,21 @@
 //   phase 2  takes tickets from word kTicketB: prefill items first, then decode
 //            slices; none of them waits for another workgroup.
 //   leave    the workgroup that leaves last (word kExited) clears words
-//            0 .. kFault - 1, so the next call finds them zero.
+//            0 .. kFault - 1 (and the GPU's append shards), so the next call
+//            finds them zero.
 #pragma once
 
 namespace qknr {
 
 // control words at the start of the step's workspace (kFault and the two words
-// after it are written only when a wait gives up, and never cleared)
+// after it are written only when a wait gives up, and never cleared). The GPU
+// counts kAppendDone in kAppendShards counters kShardStride ints apart from
+// kShardBase (a workgroup adds to shard blockIdx % kAppendShards, the wait sums
+// them): one counter that 264 append items add to while the finished workgroups
+// poll it took about 100 us per add.
 enum : int { kTicketA = 0, kAppendDone, kPlanDone, kTicketB, kExited, kFault, kSeenAppend, kSeenPlan,
-             kCtlInts = 64 };
+             kShardBase = 64, kShardStride = 256, kAppendShards = 8,
+             kCtlInts = kShardBase + kShardStride * kAppendShards };
 
 struct StepWork {
   int n_append_items;    // phase 1: ticket 0 = the plan, tickets 1 .. n_append_items = append chunks
@@ -39,13 +46,15 @@ struct StepWork {
 // Env provides, each called by every thread of a workgroup and returning the same
 // value in every thread:
 //   int  take(int word)        one atomic add of 1 to `word`; its old value
-//   void publish(int word)     the workgroup's stores are complete, then one
-//                              release add of 1 to `word`
+//   void publish(int word)     the workgroup's stores are complete where every
+//                              workgroup reads them, then one add of 1 to
+//                              `word` (the kernel's items store write-through and
+//                              add relaxed; the host model adds with a release)
 //   bool wait_ready(int n_append, int n_plan)
 //                              until kAppendDone >= n_append and kPlanDone >=
 //                              n_plan, bounded; true with an acquire when reached,
 //                              false (fault recorded) when the bound ran out
-//   int  leave()               one acquire-release add of 1 to kExited; its old value
+//   int  leave()               one add of 1 to kExited; its old value
 //   void clear()               words 0 .. kFault - 1 set to zero
 //   void plan(), append(int), prefill(int), decode(int)    the items
 template <class Env>

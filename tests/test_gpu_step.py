@@ -36,10 +36,13 @@ def _need_gpu():
     torch.cuda.empty_cache()
 
 
+CTL_INTS = 64 + 256 * 8   # the control area: 64 words, then 8 append counters 256 ints apart
+
+
 def _control_words_clear(ws):
-    words = ws[:64 * 4].view(torch.int32).cpu().numpy()
+    words = ws[:CTL_INTS * 4].view(torch.int32).cpu().numpy()
     assert words[5] == 0, f"a workgroup gave up waiting for the writes (saw {words[6]}, {words[7]})"
-    assert not words.any(), f"control words not cleared: {words[:8]}"
+    assert not words.any(), f"control words not cleared: {words[:8]}, counters {words[64::256]}"
 
 
 def _fused(w, ws=None, keep_pre=True):
