@@ -5,7 +5,8 @@
 //
 // One persistent kernel, one workgroup of 8 waves per CU, running the work protocol
 // of step_protocol.h: phase 1 takes the plan (ticket 0: sorts the prefill tiles by
-// cost) and the append chunks (16 tokens each, one token per 256-thread half);
+// cost) and the append chunks (at least 16 tokens each and at most one per
+// workgroup, one token per 256-thread half);
 // after every phase-1 item has published, phase 2 takes prefill work items in plan
 // order, then decode slices, so the two kernels' tails overlap.
 // Visibility across XCDs (each has its own L2): the phase-1 items write with
@@ -30,7 +31,7 @@ namespace qknr {
 namespace {
 
 constexpr int kStepThreads = 512;
-constexpr int kAppendPerItem = 16;          // tokens per append item
+constexpr int kAppendMinPerItem = 16;       // tokens per append item at least
 constexpr int kPlanCap = kTabCache / 2;     // tiles the in-kernel plan sorts (keys in the page-id cache)
 constexpr int kStepMaxRows = 8192;          // decode rows (LDS prefix table)
 constexpr uint64_t kWaitTicks = 100000000;  // wait bound: 1 s of the 100 MHz real-time counter
@@ -47,6 +48,7 @@ struct StepParams {
   int64_t num_pages;
   uint16_t *q_out, *k_pool, *v_pool;
   StepWork work;
+  int append_per_item;   // tokens per append item (even)
   PrefillParams pre;
   int n_tiles;
   int* order;   // plan output (null: tiles in pack order)
@@ -149,8 +151,8 @@ struct DeviceEnv {
   }
 
   __device__ void append(int chunk) {
-    const int t0 = chunk * kAppendPerItem;
-    for (int i = tid >> 8; i < kAppendPerItem; i += 2) {
+    const int t0 = chunk * S.append_per_item;
+    for (int i = tid >> 8; i < S.append_per_item; i += 2) {
       const int t = t0 + i;
       if (t >= S.n_tokens) break;
       append_token<uint16_t, uint16_t, false, false, true>(
@@ -239,7 +241,15 @@ hipError_t launch_step(hipStream_t stream, const StepArgs& a) {
   S.q_out = (uint16_t*)a.q_out;
   S.k_pool = (uint16_t*)a.k_pool;
   S.v_pool = (uint16_t*)a.v_pool;
-  S.work.n_append_items = (S.n_tokens + kAppendPerItem - 1) / kAppendPerItem;
+  // Append items: at least 16 tokens, and at most one per workgroup besides the
+  // one that takes the plan, so that no workgroup runs two while others wait for
+  // them (a workgroup runs an item's tokens two at a time, one per 256-thread half).
+  const int grid = step_grid(R);
+  {
+    const int per = std::max(kAppendMinPerItem, (S.n_tokens + std::max(grid - 1, 1) - 1) / std::max(grid - 1, 1));
+    S.append_per_item = (per + 1) & ~1;
+  }
+  S.work.n_append_items = (S.n_tokens + S.append_per_item - 1) / S.append_per_item;
   S.ctl = reinterpret_cast<int*>(ws);
   S.order = (n_tiles > 0 && n_tiles <= kPlanCap) ? reinterpret_cast<int*>(ws + kCtlInts * sizeof(int)) : nullptr;
   S.n_tiles = n_tiles;
@@ -268,7 +278,6 @@ hipError_t launch_step(hipStream_t stream, const StepArgs& a) {
   Pp.partials = nullptr;
   Pp.partial_ml = nullptr;
 
-  const int grid = step_grid(R);
   DecodeParams& D = S.dec;
   const size_t dec_off = kCtlInts * sizeof(int) + align256((size_t)n_tiles * sizeof(int));
   const size_t pairs = (size_t)R * a.n_kv_heads;
