@@ -132,11 +132,15 @@ __device__ __forceinline__ void append_token(
   // Every load the position does not decide goes out with the position's: the
   // first two head vectors of the lane's group (hv = grp, grp + 32), its first
   // piece of v and a caller-given slot. Only the page table and the rotation's
-  // cos/sin wait for the position.
+  // cos/sin wait for the position. The whole-vector norm leaves its head vectors
+  // to the cache instead: it reads them in two passes around a barrier, and
+  // holding them in registers costs it a workgroup per CU (36.5 -> 40.8 us on
+  // 4224 tokens).
   const int pos = t < n_first ? positions[t] : positions2[t - n_first];
+  constexpr int kHeld = WHOLE ? 0 : 2;   // head vectors held from the start
   RawIn ra[2] = {}, rb[2] = {}, rv = {};
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kHeld; ++u) {
     const int hv = grp + 32 * u;
     if (hv < n_norm) {
       ra[u] = VIn::load_raw(source(hv) + 8 * j);
@@ -198,10 +202,10 @@ __device__ __forceinline__ void append_token(
   // the first two iterations' were loaded at the start
   auto fetch = [&](int hv, float (&a)[8], float (&b)[8]) {
     const int it = (hv - grp) >> 5;
-    if (it == 0) {
+    if (kHeld > 0 && it == 0) {
       VIn::unpack(ra[0], a);
       VIn::unpack(rb[0], b);
-    } else if (it == 1) {
+    } else if (kHeld > 1 && it == 1) {
       VIn::unpack(ra[1], a);
       VIn::unpack(rb[1], b);
     } else {
