@@ -271,6 +271,27 @@ def measure_hbm_reference(Q, dev, reps=5):
             "source": "qkr_read_probe over 4 GiB (read); torch copy_ over 1 GiB (read + write); HIP events"}
 
 
+def measure_mfma_reference(Q, dev, iters=4000, reps=5):
+    """What the matrix cores sustain on this GPU: the library's MFMA probe (bf16
+    32x32x16 MFMAs from registers, eight independent accumulators per wave, two
+    waves per SIMD, no memory traffic). The roofline peak stays the published
+    2.5 PFLOP/s dense bf16."""
+    import torch
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    Q.mfma_probe(iters, sink)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    flops = 0
+    for _ in range(reps):
+        flops += Q.mfma_probe(iters, sink)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "source": "qkr_mfma_probe: bf16 32x32x16 MFMAs from registers on every CU, HIP events"}
+
+
 def measure_append_steady(step, stream, reps=50):
     """The step's append, launched back to back (its in-step event window also holds
     the launch gap after the previous step's last kernel)."""
@@ -607,6 +628,7 @@ def main():
     packed = measure_packed(step, stream) if (step.P and extras) else None
     variants = measure_variants(step, stream) if extras else None
     hbm_ref = measure_hbm_reference(Q, dev) if extras else None
+    mfma_ref = measure_mfma_reference(Q, dev) if extras else None
     others = None
     if extras and args.workload == 4 and args.kv_heads == 8:
         others = {}
@@ -680,6 +702,10 @@ def main():
         if roofline["unit"] == "GB/s":
             hbm_ref["decode_frac_of_read"] = round(roofline["achieved"] / hbm_ref["read_gbs"], 4)
         result["hbm_reference"] = hbm_ref
+    if mfma_ref is not None:
+        if "prefill" in result:
+            mfma_ref["prefill_frac_of_probe"] = round(result["prefill"]["tflops"] / mfma_ref["tflops"], 4)
+        result["mfma_reference"] = mfma_ref
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, snap)
     print(json.dumps(result), flush=True)

@@ -425,6 +425,18 @@ int qkr_rope_table(double theta, int32_t rope_rows, int32_t head_dim,
  */
 int qkr_read_probe(void* stream, const void* buf, size_t bytes, float* out);
 
+/*
+ * qkr_mfma_probe -- measurement helper, not part of the attention path: one kernel
+ * of `iters` rounds of eight independent bf16 32x32x16 MFMAs per wave, eight waves
+ * on every CU, with no memory traffic in the loop, enqueued on `stream`. Timing it
+ * gives the dense bf16 rate the matrix cores sustain on this GPU, a practical
+ * ceiling to set beside the published MFMA peak. *flops (host) receives the FLOPs
+ * the kernel performs; `out` (device, 1 float) is written only in the practically
+ * impossible case that the accumulators sum to a fixed sentinel. QKR_EINVAL for a
+ * null pointer or a negative count.
+ */
+int qkr_mfma_probe(void* stream, int32_t iters, float* out, int64_t* flops);
+
 /* Human-readable name of a qkr_status value. */
 const char* qkr_status_str(int status);
 

@@ -8,7 +8,7 @@ raises ImportError there.
 """
 _NAMES = (
     "EXPORTED", "LIB_PATH", "QKR_EDATA", "check_indices", "QKR_BF16", "QKR_F32", "QknrError", "decode_workspace_bytes", "decode_kernel_name",
-    "last_error", "packed_prefill_attn", "packed_workspace_bytes", "paged_decode_attn", "paged_decode_attn_noalloc",
+    "last_error", "mfma_probe", "packed_prefill_attn", "packed_workspace_bytes", "paged_decode_attn", "paged_decode_attn_noalloc",
     "paged_prefill_attn", "pool_desc", "prefill_workspace_bytes",
     "qknorm_rope_append", "read_probe", "rope_table", "status_str", "step_paged", "step_workspace_bytes", "version",
 )

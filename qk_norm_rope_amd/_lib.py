@@ -40,6 +40,7 @@ EXPORTED = (
     "step_paged_workspace",
     "qkr_check_indices",
     "qkr_read_probe",
+    "qkr_mfma_probe",
     "qkr_rope_table",
     "qkr_status_str",
     "qkr_last_error",
@@ -137,6 +138,8 @@ def _load():
     lib.qkr_status_str.argtypes = [ctypes.c_int]
     lib.qkr_last_error.restype = ctypes.c_char_p
     lib.qkr_last_error.argtypes = []
+    lib.qkr_mfma_probe.restype = ctypes.c_int
+    lib.qkr_mfma_probe.argtypes = [vp, i32, vp, ctypes.POINTER(ctypes.c_int64)]
     lib.qkr_read_probe.restype = ctypes.c_int
     lib.qkr_read_probe.argtypes = [vp, vp, sz, vp]
     lib.qkr_version.restype = ctypes.c_int
@@ -427,6 +430,19 @@ def read_probe(buf, out, stream=None) -> None:
     s = stream if stream is not None else torch.cuda.current_stream()
     _check(LIB.qkr_read_probe(ctypes.c_void_p(s.cuda_stream), ctypes.c_void_p(buf.data_ptr()),
                               buf.numel() * buf.element_size(), ctypes.c_void_p(out.data_ptr())), "qkr_read_probe")
+
+
+def mfma_probe(iters, out, stream=None) -> int:
+    """qkr_mfma_probe: a loop of bf16 MFMAs on every CU (a measurement helper, not
+    part of the attention path); out: 1 float32 on the device. Returns the FLOPs."""
+    import torch
+    if not out.is_cuda or out.dtype != torch.float32 or out.numel() < 1:
+        raise ValueError("mfma_probe needs one device float32")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    flops = ctypes.c_int64(0)
+    _check(LIB.qkr_mfma_probe(ctypes.c_void_p(s.cuda_stream), int(iters), ctypes.c_void_p(out.data_ptr()),
+                              ctypes.byref(flops)), "qkr_mfma_probe")
+    return int(flops.value)
 
 
 def version() -> int:

@@ -102,6 +102,14 @@ extern "C" {
 
 int qkr_version(void) { return 100; }
 
+int qkr_mfma_probe(void* stream, int32_t iters, float* out, int64_t* flops) {
+  if (!out || !flops || iters < 0) return QKR_EINVAL;
+  long long f = 0;
+  const int st = launch_status(qknr::launch_mfma_probe(static_cast<hipStream_t>(stream), iters, out, &f));
+  *flops = st == QKR_OK ? (int64_t)f : 0;
+  return st;
+}
+
 int qkr_read_probe(void* stream, const void* buf, size_t bytes, float* out) {
   if (!buf || !out || (reinterpret_cast<uintptr_t>(buf) & 15) != 0 || bytes % 16 != 0) return QKR_EINVAL;
   if (bytes == 0) return QKR_OK;

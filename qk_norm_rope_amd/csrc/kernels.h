@@ -111,6 +111,8 @@ struct CheckArgs {
 };
 // plain streaming read of bytes (a multiple of 16) at buf, 16-byte aligned
 hipError_t launch_read_probe(hipStream_t stream, const void* buf, size_t bytes, float* out);
+// `iters` rounds of 8 bf16 32x32x16 MFMAs per wave, 8 waves per CU; *flops: the FLOPs enqueued
+hipError_t launch_mfma_probe(hipStream_t stream, int iters, float* out, long long* flops);
 
 hipError_t launch_check_indices(hipStream_t stream, const CheckArgs& a);
 

@@ -1,7 +1,8 @@
-// HBM read-rate reference: a plain streaming read with nothing of the attention
-// path in it (no paging, masking or arithmetic beyond a sum), so that a measured
-// bandwidth can be set beside what the same GPU reaches on the simplest possible
-// read, as well as beside the published peak.
+// Rate references: a plain streaming read with nothing of the attention path in it
+// (no paging, masking or arithmetic beyond a sum), and a loop of bf16 MFMAs with
+// no memory traffic, so that measured bandwidth and FLOP/s can be set beside what
+// the same GPU reaches on the simplest kernels, as well as beside the published
+// peaks.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,7 +28,46 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const float4* __restric
   if (s == -1.2345678e-30f) out[0] = s;
 }
 
+// Eight independent 32x32x16 bf16 MFMA accumulators per wave, `iters` rounds of
+// eight MFMAs with no memory traffic in the loop: the dense bf16 rate the matrix
+// cores sustain with every SIMD busy (two waves per SIMD).
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void mfma_probe_kernel(int iters, float* __restrict__ out) {
+  const int l = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (float)((l + i) & 7));
+    b[i] = (__bf16)(0.001f * (float)((l * 3 + i) & 7));
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[k][i] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[k][i];
+  if (s == -1.2345678e-30f) out[0] = s;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_probe(hipStream_t stream, int iters, float* out, long long* flops) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  // one 8-wave workgroup per CU
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(cus), dim3(512), 0, stream, iters, out);
+  *flops = (long long)cus * 8 * (long long)iters * 8 * (32LL * 32 * 16 * 2);
+  return hipGetLastError();
+}
 
 hipError_t launch_read_probe(hipStream_t stream, const void* buf, size_t bytes, float* out) {
   int dev = 0, cus = 0;

@@ -184,6 +184,14 @@ def test_read_probe_host_checks():
     assert lib.qkr_read_probe(None, ctypes.c_void_p(0x1000), 0, ctypes.c_void_p(0x1000)) == 0     # nothing to read
 
 
+def test_mfma_probe_host_checks():
+    lib = L.LIB
+    flops = ctypes.c_int64(0)
+    assert lib.qkr_mfma_probe(None, 10, None, ctypes.byref(flops)) == -1             # null out
+    assert lib.qkr_mfma_probe(None, 10, ctypes.c_void_p(0x1000), None) == -1        # null flops
+    assert lib.qkr_mfma_probe(None, -1, ctypes.c_void_p(0x1000), ctypes.byref(flops)) == -1   # negative count
+
+
 def test_rope_table_rejects_bad_arguments():
     buf = np.zeros(4, np.float32)
     p = buf.ctypes.data_as(ctypes.c_void_p)
