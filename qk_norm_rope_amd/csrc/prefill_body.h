@@ -567,36 +567,57 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const int i
             st[kt][rg] = (kk <= lim && kk >= low) ? st[kt][rg] : -INFINITY;
           }
       }
-      float mx = -INFINITY;
+      // exp2 of the page's scaled scores against the shift ms into pb (bf16);
+      // returns the lane's sum of them (four chains keep the additions independent)
+      auto exp_page = [&](float ms) {
+        float ps4[4];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int c = 0; c < 4; ++c) {
 #pragma unroll
-        for (int rg = 0; rg < 16; ++rg) mx = fmaxf(mx, st[kt][rg]);
-      {
-        // the other half of the query's keys sits in lane l ^ 32. The swap's two
-        // results are read by value (__uint_as_float): a __builtin_bit_cast of an
-        // element of the returned vector reads element 0 for either index (seen in
-        // the front end's IR), which dropped the other half from the page max.
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc;
-      }
-      const bool need = mx > m + kRescaleThreshold;
-      const float mn = need ? mx : m;
-      const float corr = need ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
-      const float ms = (mn == -INFINITY) ? 0.f : mn;
-      // four partial sums keep the additions independent
-      float ps4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-          const int rg = 4 * (2 * (c & 1) + (ii >> 2)) + (ii & 3);
-          const float ev = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][rg], sc, -ms));
-          ps4[ii & 3] += ev;
-          pb[c][ii] = (__bf16)ev;
+          for (int ii = 0; ii < 8; ++ii) {
+            const int rg = 4 * (2 * (c & 1) + (ii >> 2)) + (ii & 3);
+            const float ev = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][rg], sc, -ms));
+            if (c == 0 && ii < 4) ps4[ii] = ev;
+            else ps4[ii & 3] += ev;
+            pb[c][ii] = (__bf16)ev;
+          }
         }
+        return (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+      };
+      // The page against the running max as it stands. A lane whose sum stays at
+      // most 2^7 has no score above m + 7, so its query's max cannot have risen past
+      // m + kRescaleThreshold and the page max is not needed. Only when some lane's
+      // sum is larger, or from the start while a query of the wave has no finite max
+      // yet, does the wave take the page max and compute the page against the max
+      // that results. Either way the result is the one taking the max first gives,
+      // bit for bit.
+      float ps = 0.f;
+      bool slow = __any(m == -INFINITY);
+      if (!slow) {
+        ps = exp_page(m);
+        slow = __any(!(ps <= 128.f));
       }
-      const float ps = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+      float mn = m, corr = 1.f;
+      bool need = false;
+      if (slow) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int rg = 0; rg < 16; ++rg) mx = fmaxf(mx, st[kt][rg]);
+        {
+          // the other half of the query's keys sits in lane l ^ 32. The swap's two
+          // results are read by value (__uint_as_float): a __builtin_bit_cast of an
+          // element of the returned vector reads element 0 for either index (seen in
+          // the front end's IR), which dropped the other half from the page max.
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc;
+        }
+        need = mx > m + kRescaleThreshold;
+        mn = need ? mx : m;
+        corr = need ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
+        ps = exp_page(mn == -INFINITY ? 0.f : mn);
+      }
       lsum = lsum * corr + ps;
       m = mn;
       if (__any(need)) {
