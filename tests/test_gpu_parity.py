@@ -112,7 +112,7 @@ def test_decode_every_output_with_two_rounds_of_workgroups():
     report("two-round decode", run.dec_out.cpu().numpy(), oracle_decode(w, ref_q, kp, vp), TOL_BF16)
 
 
-RAGGED_DECODE = [0, 1, 2, 15, 16, 63, 64, 65, 127, 128, 129, 1000, 4095]
+RAGGED_DECODE = [0, 1, 2, 15, 16, 63, 64, 65, 127, 128, 129, 300, 1000, 3000, 4095]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -263,10 +263,11 @@ def test_decode_workspace_is_reusable():
     assert int(ws[:4 * n_pairs].view(torch.int32).abs().sum().item()) == 0
 
 
-@pytest.mark.parametrize("positions", [[0], [5, 70], [63, 64, 65], [200] * 3])
+@pytest.mark.parametrize("positions", [[0], [5, 70], [63, 64, 65], [200] * 3, [130, 300, 450]])
 def test_decode_with_fewer_pages_than_workgroups(positions):
-    # far fewer (row, KV head, page) units than resident workgroups: segments cut
-    # into single pages, many workgroups with nothing to do
+    # far fewer (row, KV head, page) units than resident workgroups: many workgroups
+    # with nothing to do; rows of 1 to 8 pages, odd counts included (a row's last
+    # 2-page chunk then holds a single page)
     dec = [(b, p) for b, p in enumerate(positions)]
     w = W.build("few_units", 26, "bf16", num_pages=64, pages_per_row=8, n_table_rows=len(dec),
                 decode=dec)
