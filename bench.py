@@ -240,7 +240,8 @@ def measure_fused(step, stream, steps, scratch):
 
 def measure_hbm_reference(Q, dev, reps=5):
     """What plain streaming kernels reach on this GPU: the library's read probe (a
-    grid-stride read, no paging, masking or attention arithmetic) over 4 GiB, and
+    grid-stride read with non-temporal loads, as decode's K/V loads; no paging,
+    masking or attention arithmetic) over 4 GiB, and
     torch's copy_ (a read and a write) over 1 GiB, both far beyond the 256 MB MALL.
     The roofline peak stays the published 8 TB/s; these say how much of it the
     simplest kernels get on the same GPU."""
@@ -268,7 +269,8 @@ def measure_hbm_reference(Q, dev, reps=5):
     torch.cuda.empty_cache()
     return {"read_gbs": round(4 * COPY_PROBE_BYTES / (read_ms * 1e-3) / 1e9, 1),
             "copy_gbs": round(2 * COPY_PROBE_BYTES / (copy_ms * 1e-3) / 1e9, 1),
-            "source": "qkr_read_probe over 4 GiB (read); torch copy_ over 1 GiB (read + write); HIP events"}
+            "source": "qkr_read_probe over 4 GiB (non-temporal read); torch copy_ over 1 GiB (read + write); "
+                      "HIP events"}
 
 
 def measure_mfma_reference(Q, dev, iters=4000, reps=5):

@@ -414,8 +414,9 @@ int qkr_rope_table(double theta, int32_t rope_rows, int32_t head_dim,
                    float* cos_out, float* sin_out);
 
 /*
- * qkr_read_probe -- measurement helper, not part of the attention path: one plain
- * streaming read of `bytes` bytes of device memory at `buf` (16-byte aligned,
+ * qkr_read_probe -- measurement helper, not part of the attention path: one
+ * streaming read (non-temporal 16-byte loads, as the decode kernel's K/V loads) of
+ * `bytes` bytes of device memory at `buf` (16-byte aligned,
  * bytes a multiple of 16), enqueued on `stream`. Timing it gives the read rate a
  * kernel with no paging, masking or attention arithmetic reaches on this GPU, a
  * practical ceiling to set beside the published HBM peak. `out` (device, 1 float)

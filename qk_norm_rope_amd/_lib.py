@@ -419,9 +419,9 @@ def check_indices(k_pool, num_q_heads: int, table, rows=None, positions=None, sl
 
 
 def read_probe(buf, out, stream=None) -> None:
-    """qkr_read_probe: one plain streaming read of the device tensor buf (a
-    measurement helper, not part of the attention path); out: 1 float32 on the
-    same device."""
+    """qkr_read_probe: one streaming read (non-temporal loads) of the device tensor
+    buf (a measurement helper, not part of the attention path); out: 1 float32 on
+    the same device."""
     import torch
     if not buf.is_cuda or not out.is_cuda or out.dtype != torch.float32 or out.numel() < 1:
         raise ValueError("read_probe needs a device buffer and one device float32")
