@@ -182,7 +182,9 @@ typedef struct qkr_attn_opts {
  * the split depends only on positions, so the result does not depend on where
  * the pages sit in the pool.
  *
- * A bfloat16 pool takes at most 12288 rows per call (QKR_EUNSUPPORTED above).
+ * A bfloat16 pool takes at most 12288 rows per call, and n_rows * num_kv_heads *
+ * (5 * pages_per_row + 12) must stay below 2^31 (the split's cost scale; 12288
+ * rows of 8 KV heads allow 4366 pages per row); beyond either, QKR_EUNSUPPORTED.
  * workspace: device memory of at least paged_decode_attn_workspace() bytes. It
  * must be zero-filled before its first use; every call leaves it ready for the
  * next (its counters return to zero). Calls that share a workspace must be

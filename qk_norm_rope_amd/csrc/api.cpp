@@ -249,6 +249,7 @@ int paged_decode_attn_ex(void* stream, const qkr_pool* pool, int32_t n_rows,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!a.bf16) return launch_status(qknr::launch_attention_generic(s, a));
   if (n_rows > qknr::decode_max_rows()) return QKR_EUNSUPPORTED;
+  if (!qknr::decode_cost_fits(n_rows, pool->num_kv_heads, pages_per_row)) return QKR_EUNSUPPORTED;
   const size_t need = qknr::decode_workspace_bytes(n_rows, pool->num_kv_heads, pages_per_row);
   if (!workspace || workspace_bytes < need) return QKR_EWORKSPACE;
   return launch_status(qknr::launch_decode_bf16(s, a));
@@ -275,6 +276,7 @@ int paged_decode_attn_noalloc(void* stream, const qkr_pool* pool, int32_t n_rows
   if (!std::isfinite(scale)) return QKR_EINVAL;
   const bool bf16 = pool->dtype == QKR_BF16;
   if (bf16 && n_rows > qknr::decode_max_rows()) return QKR_EUNSUPPORTED;
+  if (bf16 && !qknr::decode_cost_fits(n_rows, pool->num_kv_heads, pages_per_row)) return QKR_EUNSUPPORTED;
   if (bf16 && (int64_t)n_rows * pool->num_kv_heads > qknr::decode_noalloc_max_pairs()) {
     snprintf(g_last_error, sizeof(g_last_error),
              "paged_decode_attn_noalloc: %d rows x %d KV heads exceed the scratch limit of %d (row, KV head) "
@@ -437,6 +439,7 @@ int step_paged(void* stream, const qkr_pool* pool, int32_t n_prefill, int32_t n_
     if (!step_positions || !decode_out) return QKR_EINVAL;
     if (decode_row0 < 0 || (int64_t)decode_row0 + n_decode > n_table_rows) return QKR_EINVAL;
     if (n_decode > qknr::step_max_rows()) return QKR_EUNSUPPORTED;
+    if (!qknr::decode_cost_fits(n_decode, pool->num_kv_heads, pages_per_row)) return QKR_EUNSUPPORTED;
   }
   if (pages_per_row > qknr::prefill_max_pages_per_row()) return QKR_EUNSUPPORTED;
   const size_t need = qknr::step_workspace_bytes(n_prefill, n_decode, pool->num_kv_heads, pages_per_row);

@@ -12,7 +12,7 @@ namespace qknr {
 namespace {
 
 __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(DecodeParams P) {
-  extern __shared__ int s_prefix[];   // [n_rows + 1]: units before row b
+  extern __shared__ int s_prefix[];   // [n_rows + 1]: slice cost before row b
   decode_slice<4>(P, blockIdx.x, gridDim.x, s_prefix, threadIdx.x);
 }
 
@@ -344,6 +344,10 @@ size_t decode_workspace_bytes(int n_rows, int n_kv_heads, int /*pages_per_row*/)
 
 int decode_max_rows() { return kMaxRows; }
 
+bool decode_cost_fits(int n_rows, int n_kv_heads, int pages_per_row) {
+  return (int64_t)n_rows * n_kv_heads * ((int64_t)kCostA * pages_per_row + kCostB) < ((int64_t)1 << 31);
+}
+
 // Small batches take the fixed (row, KV head, chunk) grid: when the bound rows x KV
 // heads x pages per row is at most 16 pages per resident workgroup and the chunks'
 // partial states fit the workspace's partial area.
@@ -372,24 +376,19 @@ hipError_t launch_decode_bf16(hipStream_t stream, const AttnArgs& a) {
   P.gate = (const uint16_t*)a.gate;
   P.counters = static_cast<int*>(a.workspace);
   P.partials = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + counter_bytes);
-  // Large batches take two workgroups per resident slot: slices halve and the
-  // workgroups that finish first take the rest, which evens out the slices'
-  // different segment counts (64 ragged rows: 5.4 TB/s instead of 5.1). Smaller
-  // ones keep one: each workgroup pays a fixed set-up and merge, which a second
-  // round of workgroups with half the units each only repeats (128 rows at 1 KV
-  // head: 5.2 TB/s with one round, 4.4 with two; 8 rows: a chain of memory round
-  // trips that a second round lengthens). The host knows only the bound
-  // rows x KV heads x pages per row on the units; two rounds from 300 units per
-  // resident workgroup.
-  int grid = grid_for_device();
-  const int64_t bound_units = (int64_t)a.n_queries * a.n_kv_heads * a.pages_per_row;
+  // One workgroup per resident slot, each with an equal share of the cost scale
+  // (pages plus a per-segment charge), so slices with many short segments take
+  // fewer pages. With slices cut by pages alone, two rounds of workgroups had evened
+  // out their different segment counts on ragged batches; cost-cut slices in one
+  // round are faster still (64 ragged rows 244 against 259 µs, the mixed step's 128
+  // rows 628 against 645 µs), and each workgroup's set-up and merge come once.
+  const int grid = grid_for_device();
   if (decode_uses_small_kernel(a.n_queries, a.n_kv_heads, a.pages_per_row)) {
     const int chunks = (a.pages_per_row + kChunkPages - 1) / kChunkPages;
     const int64_t small_grid = (int64_t)a.n_queries * a.n_kv_heads * chunks;
     hipLaunchKernelGGL(paged_decode_small_kernel, dim3((unsigned)small_grid), dim3(256), 0, stream, P, chunks);
     return hipGetLastError();
   }
-  if (bound_units >= 300LL * grid) grid = std::min(kMaxGrid, 2 * grid);
   const size_t lds = (size_t)(a.n_queries + 1) * sizeof(int);
   hipLaunchKernelGGL(paged_decode_bf16_kernel, dim3(grid), dim3(256), lds, stream, P);
   return hipGetLastError();

@@ -88,9 +88,18 @@ __device__ __forceinline__ float row_max16(float x) {
   return x;
 }
 
+// Slices are cut on a cost scale, not on units: a (row, KV head) segment of np pages
+// costs kCostA * np + kCostB, so that a slice holding many short segments gets fewer
+// pages (a segment's set-up, q and page-id loads and finish cost about as much as
+// 2.4 pages' streaming). A row whose position is outside its table has np = 0 but
+// keeps its kCostB per KV head, which makes a row's unit offset follow from its cost
+// offset and its index alone.
+constexpr int kCostA = 5;
+constexpr int kCostB = 12;
+
 __device__ __forceinline__ long long range_begin(int i, long long U, int G) { return (long long)i * U / G; }
 
-// workgroup whose range holds unit u
+// workgroup whose range holds point u of a range [0, U) cut into G slices
 __device__ __forceinline__ int owner(long long u, long long U, int G) {
   int i = (int)((u * G) / U);
   while (i + 1 < G && range_begin(i + 1, U, G) <= u) ++i;
@@ -105,6 +114,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 struct DecodeSeg {
   int b, pos, g, p0, pe, win, tbl;
   long long seg_begin, seg_end, stop;
+  long long cost_begin;   // the segment's first point on the slices' cost scale
   bool whole;
   bf16x8 qa[4];
 };
@@ -141,15 +151,17 @@ __device__ __forceinline__ void decode_slice(const DecodeParams& P, const int gi
   const int max_pos = P.pages_per_row * kPageSize;
   const int n_rows = P.n_rows;
 
-  // ---- units per row, exclusive prefix over rows (blocked scan)
+  // ---- cost per row, exclusive prefix over rows (blocked scan); the host keeps the
+  // total below 2^31
+  auto row_cost = [&](int p) {
+    const int np = (p >= 0 && p < max_pos) ? p / kPageSize + 1 : 0;
+    return (kCostA * np + kCostB) * P.n_kv;
+  };
   {
     const int per = (n_rows + NT - 1) / NT;
     const int b0 = tid * per;
     int local = 0;
-    for (int b = b0; b < min(b0 + per, n_rows); ++b) {
-      const int p = P.positions[b];
-      local += (p >= 0 && p < max_pos) ? (p / kPageSize + 1) * P.n_kv : 0;
-    }
+    for (int b = b0; b < min(b0 + per, n_rows); ++b) local += row_cost(P.positions[b]);
     int incl = local;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -163,49 +175,65 @@ __device__ __forceinline__ void decode_slice(const DecodeParams& P, const int gi
     int run = off + incl - local;
     for (int b = b0; b < min(b0 + per, n_rows); ++b) {
       s_prefix[b] = run;
-      const int p = P.positions[b];
-      run += (p >= 0 && p < max_pos) ? (p / kPageSize + 1) * P.n_kv : 0;
+      run += row_cost(P.positions[b]);
     }
     if (tid == NT - 1) s_prefix[n_rows] = off + incl;
     __syncthreads();
   }
-  const long long U = s_prefix[n_rows];
+  // units (row, KV head, page) before row b (each row's cost holds kCostB per KV
+  // head besides its pages, so the difference is a multiple of kCostA below 2^31)
+  auto units_before = [&](int b) -> long long {
+    return (long long)((unsigned)(s_prefix[b] - kCostB * P.n_kv * b) / (unsigned)kCostA);
+  };
+  const int C = s_prefix[n_rows];
+  const long long U = units_before(n_rows);
+  // the unit at point c < C of the cost scale, lo the last row whose prefix is <= c:
+  // in segment g of that row the first kCostB points lead to its first page, then
+  // each page takes kCostA points
+  auto unit_in_row = [&](int c, int lo) -> long long {
+    const int sc = (s_prefix[lo + 1] - s_prefix[lo]) / P.n_kv;   // a segment's cost
+    const int np = (sc - kCostB) / kCostA;
+    const int r = c - s_prefix[lo];
+    const int g = r / sc;
+    const int q = r - g * sc - kCostB;
+    return units_before(lo) + (long long)g * np + (q <= 0 ? 0 : min(np, (q + kCostA - 1) / kCostA));
+  };
+  const int top = 1 << (31 - __builtin_clz(n_rows));   // n_rows >= 1
+
   // a row without units (position outside its table) gets NaN outputs, as the
   // float32 kernel gives it: row b is written by slice b % Gd
   for (int bb = gi; bb < n_rows; bb += Gd) {
-    if (s_prefix[bb + 1] == s_prefix[bb]) {
+    if (s_prefix[bb + 1] - s_prefix[bb] == kCostB * P.n_kv) {
       float* orow = P.out + (int64_t)bb * n_q * kHeadDim;
       for (int e = tid; e < n_q * kHeadDim; e += NT) orow[e] = __builtin_nanf("");
     }
   }
-  const long long u0 = range_begin(gi, U, Gd);
-  const long long u1 = range_begin(gi + 1, U, Gd);
+  // the slice's ends on the cost scale, both rows searched in one pass
+  const int c0 = (int)range_begin(gi, C, Gd), c1 = (int)range_begin(gi + 1, C, Gd);
+  int lo0 = 0, lo1 = 0;
+  for (int st = top; st > 0; st >>= 1) {
+    if (lo0 + st < n_rows && s_prefix[lo0 + st] <= c0) lo0 += st;
+    if (lo1 + st < n_rows && s_prefix[lo1 + st] <= c1) lo1 += st;
+  }
+  const long long u0 = c0 >= C ? U : unit_in_row(c0, lo0);
+  const long long u1 = c1 >= C ? U : unit_in_row(c1, lo1);
   if (u0 >= u1) return;
 
   const int64_t pool_slots = P.num_pages * kPageSize;
-
-  // row holding u0: last b with prefix[b] <= u0
-  int b = 0;
-  {
-    int lo = 0, hi = n_rows - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= u0) lo = mid; else hi = mid - 1;
-    }
-    b = lo;
-  }
+  const int b = lo0;   // u0 lies in this row or a later one (rows without units between)
 
   // Open the segment holding unit u (row cursor bb moves forward to its row): its
   // page range in this slice, and the loads of its query operand and of the ids of
   // its first 64 pages are issued.
   auto open = [&](long long u, int& bb, DecodeSeg& sg) {
-    while (s_prefix[bb + 1] <= u) ++bb;   // skip rows without units
+    while (units_before(bb + 1) <= u) ++bb;   // skip rows without units
     sg.b = bb;
     sg.pos = P.positions[bb];
     const int np = sg.pos / kPageSize + 1;
-    const long long base = s_prefix[bb];
+    const long long base = units_before(bb);
     sg.g = (int)((u - base) / np);
     sg.p0 = (int)((u - base) % np);
+    sg.cost_begin = s_prefix[bb] + (long long)sg.g * (kCostA * np + kCostB);
     sg.seg_begin = base + (long long)sg.g * np;
     sg.seg_end = sg.seg_begin + np;
     sg.stop = min(u1, sg.seg_end);
@@ -321,7 +349,7 @@ auto compute = [&](const DecodeSeg& sg, int p, const PageRegs& r) {
     __builtin_amdgcn_wave_barrier();
   };
 
-  auto finish = [&](const DecodeSeg& sg, bool first) {
+  auto finish = [&](const DecodeSeg& sg) {
     // Finish a segment: merge the wave's lanes (DPP rotations within 16 lanes,
     // permlane swaps across the 16-lane groups: no LDS round trips), then the NW
     // waves; store the output, or the partial state and, in the last workgroup of
@@ -381,7 +409,9 @@ auto compute = [&](const DecodeSeg& sg, int p, const PageRegs& r) {
 #pragma unroll
       for (int c = 0; c < DPT; ++c) orow[c] = (A[c] / L) * gt[c];
     } else {
-      const int slot = first ? 0 : 1;
+      // slot 1: the segment goes on past this slice (the slice's last segment); slot
+      // 0: it began before the slice (its first). A slice has at most one of each.
+      const int slot = sg.stop < sg.seg_end ? 1 : 0;
       float* part = P.partials + ((int64_t)gi * 2 + slot) * kPartial + hi * (kHeadDim + 2);
       if ((tid % TPH) == 0) { store_sc1(part, M); store_sc1(part + 1, L); }
 #pragma unroll
@@ -389,11 +419,22 @@ auto compute = [&](const DecodeSeg& sg, int p, const PageRegs& r) {
       __builtin_amdgcn_s_waitcnt(0);   // the partial is at the coherence point before the ticket
       __syncthreads();
       const int rg = sg.b * P.n_kv + sg.g;
-      const int i0 = owner(sg.seg_begin, U, Gd);
-      const int i1 = owner(sg.seg_end - 1, U, Gd);
-      // workgroups with an empty range (fewer units than workgroups) add no partial
+      // the workgroups whose slices hold the segment's units: the owners of the
+      // cost points of its first and last page, and those between, whose slice ends
+      // both fall inside the segment (page index of a point there: seg_page)
+      const int np = (int)(sg.seg_end - sg.seg_begin);
+      const int i0 = owner(sg.cost_begin + kCostB, C, Gd);
+      const int i1 = owner(sg.cost_begin + kCostB + (long long)kCostA * (np - 1), C, Gd);
+      auto seg_page = [&](long long c) {
+        const long long q = c - sg.cost_begin - kCostB;
+        return q <= 0 ? 0 : (int)min((long long)np, (q + kCostA - 1) / kCostA);
+      };
+      // workgroups with an empty range (a slice inside one page's cost) add no partial
+      auto holds = [&](int i) {
+        return i == i0 || i == i1 || seg_page(range_begin(i, C, Gd)) < seg_page(range_begin(i + 1, C, Gd));
+      };
       int count = 0;
-      for (int i = i0; i <= i1; ++i) count += range_begin(i, U, Gd) < range_begin(i + 1, U, Gd);
+      for (int i = i0; i <= i1; ++i) count += holds(i);
       if (tid == 0) {
         const int old = __hip_atomic_fetch_add(&P.counters[rg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == count - 1);
@@ -401,7 +442,6 @@ auto compute = [&](const DecodeSeg& sg, int p, const PageRegs& r) {
       __syncthreads();
       if (s_last) {
         // one pass over the partials in workgroup order, 8 partials' loads in flight at a time
-        const bool i0_first = range_begin(i0, U, Gd) >= sg.seg_begin;
         float Mx = -INFINITY, Lt = 0.f, B[DPT];
 #pragma unroll
         for (int c = 0; c < DPT; ++c) B[c] = 0.f;
@@ -410,8 +450,8 @@ auto compute = [&](const DecodeSeg& sg, int p, const PageRegs& r) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const int i = ib + k;
-            const bool ok = i <= i1 && range_begin(i, U, Gd) < range_begin(i + 1, U, Gd);
-            const int slot = (i == i0 && !i0_first) ? 1 : 0;
+            const bool ok = i <= i1 && holds(i);
+            const int slot = i == i1 ? 0 : 1;   // only the last holder's slice ends in the segment
             const float* ps = P.partials + ((int64_t)(ok ? i : i0) * 2 + slot) * kPartial + hi * (kHeadDim + 2);
             mv[k] = ok ? load_sc1(ps) : -INFINITY;
             lv[k] = ok ? load_sc1(ps + 1) : 0.f;
@@ -450,7 +490,6 @@ auto compute = [&](const DecodeSeg& sg, int p, const PageRegs& r) {
     if (more) open(cur.stop, bb, nxt);
     PageRegs ra, rb;
     fetch(cur, cur.p0, ra);
-    bool first = true;
     while (true) {
       reset();
       for (int p = cur.p0; p < cur.pe; p += 2) {
@@ -461,18 +500,16 @@ auto compute = [&](const DecodeSeg& sg, int p, const PageRegs& r) {
         else if (p + 2 == cur.pe && more) fetch(nxt, nxt.p0, ra);
         if (p + 1 < cur.pe) compute(cur, p + 1, rb);
       }
-      finish(cur, first);
+      finish(cur);
       if (!more) break;
       if ((cur.pe - cur.p0) & 1) ra = rb;   // an odd page count left the next first page in rb
       cur = nxt;
-      first = false;
       more = cur.stop < u1;
       if (more) open(cur.stop, bb, nxt);
     }
   } else {
     // wave w takes pages p0 + w / 4, p0 + w / 4 + 2, ... of each segment
     long long u = u0;
-    bool first = true;
     while (u < u1) {
       DecodeSeg cur;
       open(u, bb, cur);
@@ -486,8 +523,7 @@ auto compute = [&](const DecodeSeg& sg, int p, const PageRegs& r) {
         if (p + 2 * kStride < cur.pe) fetch(cur, p + 2 * kStride, ra);
         if (p + kStride < cur.pe) compute(cur, p + kStride, rb);
       }
-      finish(cur, first);
-      first = false;
+      finish(cur);
       u = cur.stop;
     }
   }

@@ -50,6 +50,8 @@ int append_max_whole_heads();
 // Decode: split-K over page ranges with a fused last-arriver merge.
 size_t decode_workspace_bytes(int n_rows, int n_kv_heads, int pages_per_row);
 int decode_max_rows();
+// true when rows x KV heads x pages per row stay within the split's 32-bit cost scale
+bool decode_cost_fits(int n_rows, int n_kv_heads, int pages_per_row);
 hipError_t launch_decode_bf16(hipStream_t stream, const AttnArgs& a);
 // true when launch_decode_bf16 takes the (row, KV head, chunk) kernel on the current device
 bool decode_uses_small_kernel(int n_rows, int n_kv_heads, int pages_per_row);

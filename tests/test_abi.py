@@ -242,6 +242,13 @@ def test_size_limits_host_checks():
     need = lib.paged_decode_attn_workspace(ctypes.byref(pool), 12289, 4)
     assert lib.paged_decode_attn(None, ctypes.byref(pool), 12289, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
                                  0.1, FAKE, FAKE, need) == -2          # more rows than one call takes
+    # rows x KV heads x (5 x pages per row + 12) must stay below 2^31 (the decode
+    # split's cost scale): 12288 rows of 8 KV heads take 4366 pages per row, not 4367
+    need = lib.paged_decode_attn_workspace(ctypes.byref(pool), 12288, 4367)
+    assert lib.paged_decode_attn(None, ctypes.byref(pool), 12288, FAKE, FAKE, FAKE, FAKE, 4367, FAKE,
+                                 0.1, FAKE, FAKE, need) == -2
+    assert lib.paged_decode_attn_noalloc(None, ctypes.byref(pool), 12288, FAKE, FAKE, FAKE, FAKE, 4367, FAKE,
+                                         0.1, FAKE) == -2
     pneed = lib.paged_prefill_attn_workspace(ctypes.byref(pool), 100)
     assert lib.paged_prefill_attn(None, ctypes.byref(pool), 100, FAKE, FAKE, FAKE, FAKE, 3, 2049, FAKE,
                                   FAKE, 0.1, FAKE, FAKE, pneed) == -2   # longer page table than prefill takes

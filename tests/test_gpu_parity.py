@@ -93,10 +93,9 @@ def test_wide_score_range():
     report("wide scores decode", run.dec_out.cpu().numpy(), oracle_decode(w, ref_q, kp, vp), TOL_BF16)
 
 
-def test_decode_every_output_with_two_rounds_of_workgroups():
-    # rows x KV heads x pages per row above the launcher's bound for a second round
-    # of workgroups (300 units per resident workgroup on MI355X: 600 x 8 x 40 =
-    # 192000): the slices then cut many segments, with odd and even page counts
+def test_decode_every_output_on_a_large_batch():
+    # 600 rows of up to 40 pages (192000 units at most): the cost-cut slices cut
+    # many segments, with odd and even page counts, and hold many short ones whole
     rng = np.random.default_rng(48)
     n = 600
     pos = rng.integers(0, 40 * 64, size=n)
@@ -109,7 +108,7 @@ def test_decode_every_output_with_two_rounds_of_workgroups():
     ref_q, k_rows, v_rows, slots = oracle_append(w)
     check_append(run, ref_q, k_rows, v_rows, slots)
     kp, vp = oracle_pools(w, k_rows, v_rows, slots, run)
-    report("two-round decode", run.dec_out.cpu().numpy(), oracle_decode(w, ref_q, kp, vp), TOL_BF16)
+    report("large-batch decode", run.dec_out.cpu().numpy(), oracle_decode(w, ref_q, kp, vp), TOL_BF16)
 
 
 RAGGED_DECODE = [0, 1, 2, 15, 16, 63, 64, 65, 127, 128, 129, 300, 1000, 3000, 4095]

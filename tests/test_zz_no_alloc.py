@@ -41,7 +41,7 @@ def _both(run, rows):
 
 
 def test_noalloc_equals_workspace_call_on_consecutive_calls():
-    # first call: 64 ragged rows (two rounds of workgroups, many cut segments and
+    # first call: 64 ragged rows (cost-cut slices, many cut segments and
     # merges); then 8 rows, then 3 of them, on the scratch the first call left behind
     big = W.config(2)
     print(f"[noalloc] {big.name}: {big.n_decode} rows", flush=True)
