@@ -94,7 +94,7 @@ struct StepArgs {
   void *q_out, *k_pool, *v_pool;
   float *prefill_out, *decode_out;
   void* workspace;
-  int decode_slices = 0;   // decode work items (0: twice the resident workgroups)
+  int decode_slices = 0;   // decode work items (0: one per resident workgroup)
 };
 // Device-data validation: counts of index violations, kCheckCounts ints in device
 // memory (the order of QKR_CHECK_* in qknr.h).

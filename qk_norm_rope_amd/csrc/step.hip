@@ -296,7 +296,7 @@ hipError_t launch_step(hipStream_t stream, const StepArgs& a) {
   D.counters = R > 0 ? reinterpret_cast<int*>(ws + dec_off) : nullptr;
   D.partials = R > 0 ? reinterpret_cast<float*>(ws + dec_off + align256(pairs * sizeof(int))) : nullptr;
   S.work.n_decode_items =
-      R > 0 ? std::min(kMaxGrid, std::max(1, a.decode_slices > 0 ? a.decode_slices : 2 * grid)) : 0;
+      R > 0 ? std::min(kMaxGrid, std::max(1, a.decode_slices > 0 ? a.decode_slices : grid)) : 0;
   S.work.grid = grid;
 
   hipLaunchKernelGGL(step_paged_kernel, dim3(grid), dim3(kStepThreads), (size_t)(R + 1) * sizeof(int), stream, S);
