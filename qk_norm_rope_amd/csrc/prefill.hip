@@ -2,6 +2,7 @@
 // form, and one workgroup per (64-token tile, KV head) work item. The device code
 // of a work item (and its design) is in prefill_body.h.
 #include <algorithm>
+#include <climits>
 
 #include "prefill_body.h"
 #include "kernels.h"
@@ -80,6 +81,23 @@ __device__ int2 wave_scan_dpp(int v) {
   x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
   x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
   return make_int2(x - v, __builtin_amdgcn_readlane(x, 63));
+}
+
+// Maximum / minimum over the 64 lanes of a wave (every lane gets it): DPP row shifts
+// within each 16-lane row, row broadcasts across rows, then lane 63's value (lanes a
+// shift leaves without a source keep the identity passed as the old value).
+template <bool MAX>
+__device__ int wave_reduce_dpp(int v) {
+  constexpr int id = MAX ? INT_MIN : INT_MAX;
+  auto op = [](int a, int b) { return MAX ? max(a, b) : min(a, b); };
+  int x = v;
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x111, 0xf, 0xf, false));   // row_shr:1
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x112, 0xf, 0xf, false));   // row_shr:2
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x114, 0xf, 0xf, false));   // row_shr:4
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x118, 0xf, 0xf, false));   // row_shr:8
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x142, 0xa, 0xf, false));   // row_bcast:15 into rows 1, 3
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x143, 0xc, 0xf, false));   // row_bcast:31 into rows 2, 3
+  return __builtin_amdgcn_readlane(x, 63);
 }
 
 constexpr int kSplitPlanMaxTiles = 512;   // tiles for which the plan considers key splits
@@ -169,13 +187,10 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(
       const bool valid = !ok || (row[u] >= 0 && row[u] < n_table_rows && pos[u] >= 0 && pos[u] < max_pos);
       int rmin = ok ? row[u] : 0x7fffffff, rmax = ok ? row[u] : -1;
       const bool all_valid = __all(valid);
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        hi = max(hi, __shfl_xor(hi, m));
-        f = min(f, __shfl_xor(f, m));
-        rmin = min(rmin, __shfl_xor(rmin, m));
-        rmax = max(rmax, __shfl_xor(rmax, m));
-      }
+      hi = wave_reduce_dpp<true>(hi);
+      f = wave_reduce_dpp<false>(f);
+      rmin = wave_reduce_dpp<false>(rmin);
+      rmax = wave_reduce_dpp<true>(rmax);
       if (lane == 0 && i < npow2) {
         const int cost = max(hi - f, 0);
         keys[i] = i < n_tiles ? ((unsigned long long)(0xffffffffu - (unsigned)cost) << 32) | (unsigned)i : ~0ull;
