@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <climits>
 
 namespace qknr {
 
@@ -47,6 +48,24 @@ __device__ __forceinline__ float load_sc1(const float* p) {
 // Logistic function 1 / (1 + e^-x): the attention output gate (fantasma
 // "src/inference/model.zig", fullAttentionForward: attn_out *= sigmoid(gate)).
 __device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// Maximum or minimum of an int over the 64 lanes of a wave, returned to every lane:
+// DPP row shifts within each 16-lane row, then row broadcasts across rows, then lane
+// 63's value (lanes a shift leaves without a source keep the identity given as the
+// old value). No LDS round trips, unlike lane shuffles.
+template <bool MAX>
+__device__ __forceinline__ int wave_reduce_dpp(int v) {
+  constexpr int id = MAX ? INT_MIN : INT_MAX;
+  auto op = [](int a, int b) { return MAX ? max(a, b) : min(a, b); };
+  int x = v;
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x111, 0xf, 0xf, false));   // row_shr:1
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x112, 0xf, 0xf, false));   // row_shr:2
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x114, 0xf, 0xf, false));   // row_shr:4
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x118, 0xf, 0xf, false));   // row_shr:8
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x142, 0xa, 0xf, false));   // row_bcast:15 into rows 1, 3
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x143, 0xc, 0xf, false));   // row_bcast:31 into rows 2, 3
+  return __builtin_amdgcn_readlane(x, 63);
+}
 
 // Broadcast lane 0's value to the whole wave (result lives in a scalar register).
 __device__ __forceinline__ float lane0(float x) {

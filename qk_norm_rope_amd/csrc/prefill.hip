@@ -83,23 +83,6 @@ __device__ int2 wave_scan_dpp(int v) {
   return make_int2(x - v, __builtin_amdgcn_readlane(x, 63));
 }
 
-// Maximum / minimum over the 64 lanes of a wave (every lane gets it): DPP row shifts
-// within each 16-lane row, row broadcasts across rows, then lane 63's value (lanes a
-// shift leaves without a source keep the identity passed as the old value).
-template <bool MAX>
-__device__ int wave_reduce_dpp(int v) {
-  constexpr int id = MAX ? INT_MIN : INT_MAX;
-  auto op = [](int a, int b) { return MAX ? max(a, b) : min(a, b); };
-  int x = v;
-  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x111, 0xf, 0xf, false));   // row_shr:1
-  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x112, 0xf, 0xf, false));   // row_shr:2
-  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x114, 0xf, 0xf, false));   // row_shr:4
-  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x118, 0xf, 0xf, false));   // row_shr:8
-  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x142, 0xa, 0xf, false));   // row_bcast:15 into rows 1, 3
-  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x143, 0xc, 0xf, false));   // row_bcast:31 into rows 2, 3
-  return __builtin_amdgcn_readlane(x, 63);
-}
-
 constexpr int kSplitPlanMaxTiles = 512;   // tiles for which the plan considers key splits
 constexpr int kMinChunkPages = 4;          // pages of a chunk at least (a chunk's set-up is ~2 pages)
 
