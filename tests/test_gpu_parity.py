@@ -100,7 +100,7 @@ def test_decode_every_output_on_a_large_batch():
     n = 600
     pos = rng.integers(0, 40 * 64, size=n)
     pos[:8] = [0, 63, 64, 127, 128, 2559, 2495, 2496]
-    w = W.build("two_rounds", 48, "bf16", num_pages=n * 40 + 8, pages_per_row=40, n_table_rows=n,
+    w = W.build("large_batch", 48, "bf16", num_pages=n * 40 + 8, pages_per_row=40, n_table_rows=n,
                 decode=[(b, int(p)) for b, p in enumerate(pos)])
     print(f"[parity] {n} decode rows of up to 40 pages, every output", flush=True)
     run = Run(w)
