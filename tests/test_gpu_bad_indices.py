@@ -103,3 +103,34 @@ def test_prefill_tokens_with_bad_rows_positions_and_pages():
     torch.cuda.synchronize()
     assert torch.isnan(out[[125, 130, 145]]).all()
     assert torch.isfinite(out[good]).all()
+
+
+def test_decode_large_batch_with_rows_outside_their_tables():
+    # a batch for the split-K kernel (200 rows of up to 40 pages) whose positions
+    # put some rows outside their tables: the first and the last row, a run of
+    # three, and scattered ones. Such rows hold no pages but keep their per-segment
+    # charge on the slices' cost scale; every other row must still match the oracle
+    # and the bad rows must come out NaN
+    rng = np.random.default_rng(53)
+    n, ppr = 200, 40
+    pos = rng.integers(0, ppr * 64, size=n)
+    w = W.build("bad_large", 53, "bf16", num_pages=n * ppr + 8, pages_per_row=ppr, n_table_rows=n,
+                decode=[(b, int(p)) for b, p in enumerate(pos)])
+    import qk_norm_rope_amd as Q
+    assert Q.decode_kernel_name(torch.empty((8, 64, 128), dtype=torch.bfloat16, device=DEV), 32, n,
+                                ppr) == "paged_decode_bf16_kernel"
+    run = Run(w, keep_pre=False)
+    bad = [0, 17, 18, 19, 77, 150, n - 1]
+    for b in bad:
+        run.t["step_positions"][b] = -1 if b % 2 else ppr * 64 + 5
+    print(f"[bad] {n} decode rows, {len(bad)} of them outside their tables", flush=True)
+    run.step()
+    ref_q, k_rows, v_rows, slots = oracle_append(w)
+    kp, vp = oracle_pools(w, k_rows, v_rows, slots)
+    good = [b for b in range(n) if b not in bad]
+    ref = O.decode(ref_q, w.dtype, kp, vp, w.dtype, w.decode_table, w.step_positions, W.SCALE, tokens=good)
+    got = run.dec_out[good].cpu().numpy()
+    err = max_abs_err(got, ref)
+    print(f"[bad] large batch: valid rows max abs err {err:.3e}", flush=True)
+    assert err <= TOL_BF16
+    assert torch.isnan(run.dec_out[bad]).all()
