@@ -1,5 +1,6 @@
-// K2 kernel and launcher: workgroups of 4 waves, one or two per resident slot of the GPU,
-// each streaming an equal slice of the (row, KV head, page) units. The device
+// K2 kernel and launcher: workgroups of 4 waves, one per resident slot of the GPU,
+// each streaming an equal share of the (row, KV head, page) units on a cost scale
+// that also charges each segment's set-up. The device
 // code (and its design) is in decode_body.h.
 #include <algorithm>
 #include <mutex>

@@ -11,13 +11,14 @@
 //
 // Work list: unit = (row b, KV head g, page p of the row), ordered by row, then KV
 // head, then page; a "segment" is the run of units of one (b, g). The grid G is
-// the number of workgroups the GPU holds at once (twice that for large batches),
-// and workgroup i takes units [i*U/G, (i+1)*U/G): every workgroup streams the same
-// number of 32 KB K/V page chunks, whatever the rows' lengths. A segment that lies inside one workgroup's
-// range is finished there; a segment cut by range ends yields one partial
-// softmax state (max, sum, acc) per workgroup touching it, and the last of them
-// to finish (ticket counter per segment) merges them in workgroup order, so the
-// result depends only on the positions, never on timing or on where pages sit.
+// the number of workgroups the GPU holds at once, and workgroup i takes an equal
+// share [i*C/G, (i+1)*C/G) of a cost scale on which a segment of np pages costs
+// kCostA * np + kCostB: every workgroup streams about the same number of 32 KB K/V
+// page chunks plus segment set-ups, whatever the rows' lengths. A segment that lies
+// inside one workgroup's range is finished there; a segment cut by range ends yields
+// one partial softmax state (max, sum, acc) per workgroup touching it, and the last
+// of them to finish (ticket counter per segment) merges them in workgroup order, so
+// the result depends only on the positions, never on timing or on where pages sit.
 //
 // Inside a workgroup, wave w takes keys 16w..16w+15 of each page, so each page's
 // K and V are read once for the 4 query heads of the group:
